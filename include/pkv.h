@@ -1,0 +1,178 @@
+/*
+ * pkv.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * Two device operations and their workspace query:
+ *
+ *   pkv_kv_append          writes the K/V of new tokens into their cache slots;
+ *   pkv_paged_attn_decode  single-token attention of every sequence over its
+ *                          cached context, read block by block through a
+ *                          per-sequence block table, with GQA head sharing.
+ *
+ * What they compute follows the pages this library was written from:
+ * the KV cache is cut into fixed-size blocks, logical blocks of a sequence map
+ * to physical blocks anywhere in a pool, blocks are handed out as tokens arrive
+ * ("vLLM -- PagedAttention으로 LLM 추론 성능을 2~4배 끌어올린 서빙 엔진", section
+ * "PagedAttention -- OS 가상 메모리에서 영감"); K and V of past tokens are kept
+ * per layer and head so decode only reads them (same page, sections "KV Cache가
+ * 왜 병목인가" and "Prefill vs Decode"); attention is softmax(scale q K^T) V with
+ * several q heads sharing one kv head ("[Hacker News 요약] C++와 CUDA로 vLLM의
+ * 경량 고성능 LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section "고성능 추론을 위한
+ * 고급 최적화 기법").  Block metadata (the host allocator, pkv_alloc.h) lives on
+ * the CPU and the KV tensors on the GPU ("Nano-vLLM로 배우는 vLLM 추론 엔진 작동
+ * 원리 한눈에 정리", section "KV 캐시와 Block Manager").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are device pointers to contiguous row-major memory,
+ *   16-byte aligned, owned by the caller.  The library never allocates or frees
+ *   device memory, never synchronises, and never reads device memory on the
+ *   host: it validates its scalar arguments, then enqueues kernels on `stream`
+ *   (NULL = the default stream) and returns.  Calls on different streams may
+ *   run concurrently; calls are stateless.
+ * - Element type `dtype` is PKV_BF16 or PKV_FP16 and is the same for q, the
+ *   new k/v, both caches and out.  Arithmetic is fp32.
+ * - Status: PKV_OK or a negative code (see pkv_status_str).  Argument errors
+ *   are reported before anything is enqueued; PKV_E_HIP means a launch failed.
+ *
+ * Cache layout (both caches hold N blocks of bs tokens, bs a multiple of 16;
+ * the block is the outermost index, so block n is one contiguous range):
+ *
+ *   k_cache: [N][Hkv][bs/16][D/8][16][8]   K[n,h,t,d] at
+ *            ((((n*Hkv + h)*(bs/16) + t/16)*(D/8) + d/8)*16 + t%16)*8 + d%8
+ *   v_cache: [N][Hkv][bs/16][D][16]        V[n,h,t,d] at
+ *            (((n*Hkv + h)*(bs/16) + t/16)*D + d)*16 + t%16
+ *
+ * i.e. every (block, kv head) is split into 16-token sub-tiles of 16*D
+ * elements; inside a K sub-tile, 8 consecutive dims of one token form a
+ * 16-byte run and the runs of the 16 tokens follow each other; inside a V
+ * sub-tile, the 16 token values of one dim are contiguous.  A slot is
+ * n*bs + t (block n, token t of the block).
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "pkv_status.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { PKV_BF16 = 0, PKV_FP16 = 1 };
+
+/* Decode kernel selection for pkv_paged_attn_decode_ex. */
+enum { PKV_IMPL_AUTO = 0, PKV_IMPL_SIMT = 1, PKV_IMPL_MFMA = 2 };
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_str(int status);
+
+/*
+ * pkv_kv_append -- store the K and V of num_tokens new tokens.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim]
+ *   slot_mapping  [num_tokens] int64: slot of each token; a negative slot means
+ *                 "padding token, write nothing"; a slot >= num_blocks*block_size
+ *                 is ignored as well (never written).  Non-negative slots must be
+ *                 distinct (caller precondition; with duplicates the surviving
+ *                 value is unspecified).
+ *   k_cache, v_cache  the pools described above, updated in place.  Only the
+ *                 bytes of the written slots change.
+ *
+ * Supported: head_dim a multiple of 8 up to 512, block_size a multiple of 16
+ * up to 1024, any number of kv heads.  The copy is bit-exact.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (negative sizes, misaligned pointers),
+ * PKV_E_UNSUPPORTED, PKV_E_HIP.
+ */
+int pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                  void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype, hipStream_t stream);
+
+/*
+ * pkv_decode_workspace_bytes -- device workspace that pkv_paged_attn_decode
+ * needs for these sizes (0 when the context fits one partition).  The _ex form
+ * takes the same partition_tokens as pkv_paged_attn_decode_ex.
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len);
+size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                     int32_t partition_tokens);
+
+/*
+ * pkv_paged_attn_decode -- out = softmax(scale * q K^T) V for each sequence.
+ *
+ *   q             [num_seqs][num_q_heads][head_dim]: the query of the token
+ *                 being decoded.  q head h reads kv head h / G, G = Hq / Hkv.
+ *   k_cache, v_cache  pools of num_blocks blocks (layout above).
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32: physical block of each
+ *                 logical block.  Entries at or past ceil(L_i / block_size) are
+ *                 never read.
+ *   context_lens  [num_seqs] int32: L_i, the number of cached tokens attended
+ *                 to (positions 0 .. L_i-1; includes the token appended this
+ *                 step).  Tail slots of a last block and unused blocks may hold
+ *                 anything, NaN included: they never reach the output.
+ *   max_context_len  host-side upper bound of every L_i; must not exceed
+ *                 max_blocks_per_seq * block_size.  Sizes the partitioning.
+ *   scale         softmax scale (typically 1/sqrt(head_dim)).
+ *   out           [num_seqs][num_q_heads][head_dim], written in `dtype`
+ *                 (fp32 result rounded to nearest even).
+ *   workspace     device scratch of at least pkv_decode_workspace_bytes(...)
+ *                 bytes (may be NULL when that is 0).  Contents on entry do
+ *                 not matter; it holds per-partition partial results.
+ *
+ * Result for a sequence with L_i = 0: zeros.  A sequence whose L_i is
+ * negative, above max_context_len or above max_blocks_per_seq * block_size,
+ * or whose table names a block outside [0, num_blocks), gets NaN in the
+ * affected heads instead of a memory access outside the pool.
+ *
+ * Supported: head_dim 64 or 128; block_size a multiple of 16 up to 1024;
+ * G in {1, 2, 4, 8, 16} (the SIMT kernel: G * head_dim <= 512).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE, PKV_E_UNSUPPORTED, PKV_E_WORKSPACE, PKV_E_HIP.
+ */
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_paged_attn_decode_ex -- as above, with two tuning knobs:
+ *   partition_tokens  0 = automatic; otherwise a multiple of 16: the context of
+ *                     each sequence is cut into partitions of this many tokens,
+ *                     each processed by its own workgroup, and the partial
+ *                     results are combined by a log-sum-exp merge pass.  A value
+ *                     >= max_context_len means a single pass without merge.
+ *   impl              PKV_IMPL_AUTO, PKV_IMPL_SIMT (vector-ALU dot products) or
+ *                     PKV_IMPL_MFMA (matrix-core tiles).
+ * Results of all choices agree to fp32 rounding.
+ */
+int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len, float scale,
+                             void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                             int32_t impl, hipStream_t stream);
+
+/*
+ * pkv_decode_plan_partition -- the partition size (tokens) the automatic choice
+ * would use for these sizes; 0 means a single pass.
+ */
+int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t max_context_len);
+
+/*
+ * pkv_decode_supported -- 1 if the decode kernel `impl` (PKV_IMPL_*) is built for
+ * this dtype, head_dim and GQA group size G = Hq / Hkv, else 0.
+ */
+int pkv_decode_supported(int32_t impl, int32_t dtype, int32_t head_dim, int32_t group);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

@@ -1,0 +1,148 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Python binding of ``libpkv.so`` (ctypes).  It only marshals arguments: torch
+tensors supply device memory and the current HIP stream, and every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, every call raises.
+
+Names mirror the C ABI in include/pkv.h and include/pkv_alloc.h:
+
+* ``kv_append(k, v, slot_mapping, k_cache, v_cache)``
+* ``paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
+* ``BlockAllocator`` -- the host-side block allocator.
+
+Caches are tensors of shape ``(num_blocks, num_kv_heads, block_size // 16, 16 * head_dim)``
+(see ``new_cache``): one row per 16-token sub-tile of a (block, kv head),
+with elements placed as include/pkv.h describes.
+"""
+import ctypes
+import os
+
+import torch
+
+from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
+
+__all__ = ["kv_append", "paged_attn_decode", "decode_workspace_bytes", "decode_supported", "plan_partition", "new_cache",
+           "cache_dims", "BlockAllocator", "PkvError", "lib"]
+
+_DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
+IMPLS = {"auto": 0, "simt": 1, "mfma": 2}
+
+
+def _dtype_code(t):
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise PkvError(f"unsupported dtype {t.dtype}; use bfloat16 or float16") from None
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise PkvError(msg)
+
+
+def _device_tensor(t, name, dtype=None, ndim=None):
+    _need(isinstance(t, torch.Tensor), f"{name} must be a torch tensor")
+    _need(t.is_cuda, f"{name} must be on a GPU")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+    if dtype is not None:
+        _need(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None:
+        _need(t.dim() == ndim, f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+def new_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat16, device="cuda"):
+    """Uninitialised K or V pool in the library's layout."""
+    _need(block_size % 16 == 0, "block_size must be a multiple of 16")
+    return torch.empty((num_blocks, num_kv_heads, block_size // 16, 16 * head_dim), dtype=dtype, device=device)
+
+
+def cache_dims(cache):
+    """(num_blocks, num_kv_heads, block_size, head_dim) of a pool made by new_cache."""
+    _need(cache.dim() == 4 and cache.shape[3] % 16 == 0, f"bad cache shape {tuple(cache.shape)}")
+    n, h, s, e = cache.shape
+    return int(n), int(h), int(s) * 16, int(e) // 16
+
+
+def kv_append(k, v, slot_mapping, k_cache, v_cache):
+    """Write k/v ([T, Hkv, D]) into the slots ``slot_mapping`` (int64 [T]) of the pools."""
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    for name, t in (("k", k), ("v", v)):
+        _device_tensor(t, name, k_cache.dtype, 3)
+        _need(tuple(t.shape[1:]) == (Hkv, D), f"{name} must be [T, {Hkv}, {D}], got {tuple(t.shape)}")
+    _need(k.shape == v.shape, "k and v differ in shape")
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+    _need(slot_mapping.shape[0] == k.shape[0], "slot_mapping must have one slot per token")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _device_tensor(t, name)
+    check(lib().pkv_kv_append(_ptr(k), _ptr(v), _ptr(slot_mapping), k.shape[0], _ptr(k_cache), _ptr(v_cache),
+                              N, bs, Hkv, D, _dtype_code(k_cache), _stream(k_cache)))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                           partition_tokens=0):
+    return int(lib().pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                   max_context_len, partition_tokens))
+
+
+def decode_supported(impl, dtype, head_dim, group):
+    """Whether decode kernel ``impl`` ("auto", "simt", "mfma") is built for these sizes."""
+    code = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else {"bf16": PKV_BF16, "fp16": PKV_FP16}[dtype]
+    return bool(lib().pkv_decode_supported(IMPLS[impl], code, int(head_dim), int(group)))
+
+
+def plan_partition(num_seqs, num_kv_heads, block_size, max_context_len):
+    return int(lib().pkv_decode_plan_partition(num_seqs, num_kv_heads, block_size, max_context_len))
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, *,
+                      max_context_len=None, workspace=None, partition_tokens=0, impl="auto"):
+    """softmax(scale q K^T) V per sequence over its paged context.
+
+    q: [B, Hq, D]; block_tables: int32 [B, M]; context_lens: int32 [B] (device);
+    max_context_len: host-side bound of every length (default M * block_size);
+    workspace: uint8 device tensor of at least decode_workspace_bytes(...) bytes
+    (allocated through torch when omitted).  Returns ``out`` ([B, Hq, D]).
+    """
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(q, "q", k_cache.dtype, 3)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    _device_tensor(k_cache, "k_cache")
+    _device_tensor(v_cache, "v_cache")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    _need(impl in IMPLS, f"impl must be one of {sorted(IMPLS)}")
+    check(lib().pkv_paged_attn_decode_ex(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
+        ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N, _dtype_code(q), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), int(partition_tokens), IMPLS[impl], _stream(q)))
+    return out
+
+
+from .allocator import BlockAllocator  # noqa: E402

@@ -1,0 +1,69 @@
+"""Loading libpkv.so and declaring its C prototypes (ctypes)."""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+PKV_BF16 = 0
+PKV_FP16 = 1
+
+_c = ctypes
+_vp = _c.c_void_p
+_i32 = _c.c_int32
+_i64 = _c.c_int64
+
+# name -> (restype, argtypes); the order follows include/pkv.h and include/pkv_alloc.h
+PROTOTYPES = {
+    "pkv_status_str": (_c.c_char_p, [_c.c_int]),
+    "pkv_kv_append": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_decode_workspace_bytes": (_c.c_size_t, [_i32] * 6),
+    "pkv_decode_workspace_bytes_ex": (_c.c_size_t, [_i32] * 7),
+    "pkv_paged_attn_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _vp]),
+    "pkv_paged_attn_decode_ex": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _i32, _i32, _vp]),
+    "pkv_decode_plan_partition": (_i32, [_i32] * 4),
+    "pkv_decode_supported": (_c.c_int, [_i32] * 4),
+    "pkv_alloc_create": (_vp, [_i32, _i32, _c.c_uint64]),
+    "pkv_alloc_destroy": (None, [_vp]),
+    "pkv_alloc_add_seq": (_c.c_int, [_vp, _i64, _i32]),
+    "pkv_alloc_add_seq_shared": (_c.c_int, [_vp, _i64, _i32, _i64, _i32]),
+    "pkv_alloc_append_slot": (_c.c_int, [_vp, _i64, _vp]),
+    "pkv_alloc_append_slots": (_c.c_int, [_vp, _vp, _i32, _vp]),
+    "pkv_alloc_free_seq": (_c.c_int, [_vp, _i64]),
+    "pkv_alloc_block_tables": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "pkv_alloc_num_free": (_i32, [_vp]),
+    "pkv_alloc_num_seqs": (_i32, [_vp]),
+    "pkv_alloc_context_len": (_c.c_int, [_vp, _i64, _vp]),
+    "pkv_alloc_refcount": (_i32, [_vp, _i32]),
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PkvError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_448_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in PROTOTYPES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def check(status):
+    if status != 0:
+        raise PkvError(f"libpkv: {lib().pkv_status_str(status).decode()} (status {status})", status)
+    return status

@@ -1,0 +1,205 @@
+// Host-side block allocator: a free list of physical block ids, per-block
+// reference counts and per-sequence block lists.  Produces block tables,
+// context lengths and slots; never touches device memory.
+//
+// Paging semantics as on the vLLM page ("vLLM -- PagedAttention으로 LLM 추론 성능을
+// 2~4배 끌어올린 서빙 엔진", section "PagedAttention -- OS 가상 메모리에서 영감":
+// blocks taken only as tokens arrive, non-contiguous physical blocks behind a
+// contiguous logical sequence, free blocks reusable by any request) and the
+// Nano-vLLM page ("Nano-vLLM로 배우는 vLLM 추론 엔진 작동 원리 한눈에 정리",
+// section "KV 캐시와 Block Manager": metadata on the CPU, shared prefix blocks).
+#include "pkv_alloc.h"
+
+#include <algorithm>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+struct pkv_alloc {
+  struct Seq {
+    std::vector<int32_t> blocks;
+    int32_t len = 0;
+  };
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  std::vector<int32_t> free_stack;  // next block handed out is free_stack.back()
+  std::vector<int32_t> refcount;
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t take() {
+    const int32_t b = free_stack.back();
+    free_stack.pop_back();
+    refcount[b] = 1;
+    return b;
+  }
+  void release(int32_t b) {
+    if (--refcount[b] == 0) free_stack.push_back(b);
+  }
+  int32_t blocks_for(int64_t tokens) const {
+    return static_cast<int32_t>((tokens + block_size - 1) / block_size);
+  }
+};
+
+namespace {
+
+// SplitMix64 (Steele, Lea, Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the shuffle's random source.
+uint64_t splitmix64(uint64_t& state) {
+  uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, uint64_t shuffle_seed) {
+  if (num_blocks <= 0 || block_size <= 0) return nullptr;
+  pkv_alloc* a = new (std::nothrow) pkv_alloc;
+  if (!a) return nullptr;
+  try {
+    a->num_blocks = num_blocks;
+    a->block_size = block_size;
+    a->refcount.assign(num_blocks, 0);
+    // hand-out order: order[0] first
+    std::vector<int32_t> order(num_blocks);
+    for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
+    if (shuffle_seed != 0) {
+      uint64_t s = shuffle_seed;
+      for (int32_t i = num_blocks - 1; i > 0; --i) {
+        const int32_t j = static_cast<int32_t>(splitmix64(s) % static_cast<uint64_t>(i + 1));
+        std::swap(order[i], order[j]);
+      }
+    }
+    a->free_stack.assign(order.rbegin(), order.rend());
+  } catch (...) {
+    delete a;
+    return nullptr;
+  }
+  return a;
+}
+
+void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
+
+int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq_id, int32_t num_tokens) {
+  if (!a) return PKV_E_NULL;
+  if (num_tokens < 0) return PKV_E_SHAPE;
+  if (a->seqs.count(seq_id)) return PKV_E_EXISTS;
+  const int32_t need = a->blocks_for(num_tokens);
+  if (need > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  pkv_alloc::Seq s;
+  s.len = num_tokens;
+  s.blocks.reserve(need);
+  for (int32_t i = 0; i < need; ++i) s.blocks.push_back(a->take());
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t src_seq,
+                             int32_t num_shared_blocks) {
+  if (!a) return PKV_E_NULL;
+  if (num_tokens < 0 || num_shared_blocks < 0) return PKV_E_SHAPE;
+  if (a->seqs.count(seq_id)) return PKV_E_EXISTS;
+  auto it = a->seqs.find(src_seq);
+  if (it == a->seqs.end()) return PKV_E_NOSEQ;
+  const int64_t shared_tokens = static_cast<int64_t>(num_shared_blocks) * a->block_size;
+  if (shared_tokens > num_tokens || shared_tokens > it->second.len) return PKV_E_SHAPE;
+  const int32_t need = a->blocks_for(num_tokens);
+  const int32_t fresh = need - num_shared_blocks;
+  if (fresh > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  pkv_alloc::Seq s;
+  s.len = num_tokens;
+  s.blocks.reserve(need);
+  for (int32_t j = 0; j < num_shared_blocks; ++j) {
+    const int32_t b = it->second.blocks[j];
+    ++a->refcount[b];
+    s.blocks.push_back(b);
+  }
+  for (int32_t j = 0; j < fresh; ++j) s.blocks.push_back(a->take());
+  a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_alloc_append_slot(pkv_alloc* a, int64_t seq_id, int64_t* slot_out) {
+  return pkv_alloc_append_slots(a, &seq_id, 1, slot_out);
+}
+
+int pkv_alloc_append_slots(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int64_t* slots_out) {
+  if (!a || (n > 0 && (!seq_ids || !slots_out))) return PKV_E_NULL;
+  if (n < 0) return PKV_E_SHAPE;
+  // check first, so that failure changes nothing
+  std::vector<pkv_alloc::Seq*> ss(n);
+  int64_t fresh = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_E_NOSEQ;
+    ss[i] = &it->second;
+    for (int32_t k = 0; k < i; ++k)
+      if (ss[k] == ss[i]) return PKV_E_SHAPE;  // one token per sequence per call
+    if (ss[i]->len == static_cast<int64_t>(ss[i]->blocks.size()) * a->block_size) ++fresh;
+  }
+  if (fresh > static_cast<int64_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  for (int32_t i = 0; i < n; ++i) {
+    pkv_alloc::Seq& s = *ss[i];
+    const int32_t pos = s.len;
+    if (pos == static_cast<int32_t>(s.blocks.size()) * a->block_size) s.blocks.push_back(a->take());
+    slots_out[i] = static_cast<int64_t>(s.blocks[pos / a->block_size]) * a->block_size + pos % a->block_size;
+    s.len = pos + 1;
+  }
+  return PKV_OK;
+}
+
+int pkv_alloc_free_seq(pkv_alloc* a, int64_t seq_id) {
+  if (!a) return PKV_E_NULL;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_E_NOSEQ;
+  // release in reverse so the sequence's first block is the next one handed out
+  for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) a->release(*b);
+  a->seqs.erase(it);
+  return PKV_OK;
+}
+
+int pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                           int32_t pad_value, int32_t* tables_out, int32_t* context_lens_out) {
+  if (!a || (n > 0 && (!seq_ids || !tables_out || !context_lens_out))) return PKV_E_NULL;
+  if (n < 0 || max_blocks <= 0) return PKV_E_SHAPE;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end()) return PKV_E_NOSEQ;
+    if (static_cast<int32_t>(it->second.blocks.size()) > max_blocks) return PKV_E_SHAPE;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const pkv_alloc::Seq& s = a->seqs.find(seq_ids[i])->second;
+    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks;
+    const int32_t nb = static_cast<int32_t>(s.blocks.size());
+    std::copy(s.blocks.begin(), s.blocks.end(), row);
+    std::fill(row + nb, row + max_blocks, pad_value);
+    context_lens_out[i] = s.len;
+  }
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_num_free(const pkv_alloc* a) {
+  return a ? static_cast<int32_t>(a->free_stack.size()) : 0;
+}
+
+int32_t pkv_alloc_num_seqs(const pkv_alloc* a) {
+  return a ? static_cast<int32_t>(a->seqs.size()) : 0;
+}
+
+int pkv_alloc_context_len(const pkv_alloc* a, int64_t seq_id, int32_t* len_out) {
+  if (!a || !len_out) return PKV_E_NULL;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_E_NOSEQ;
+  *len_out = it->second.len;
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_refcount(const pkv_alloc* a, int32_t block) {
+  if (!a || block < 0 || block >= a->num_blocks) return -1;
+  return a->refcount[block];
+}
+
+}  // extern "C"

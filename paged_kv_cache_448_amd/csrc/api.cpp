@@ -1,0 +1,227 @@
+// C-ABI entry points of the paged KV-cache library: argument checks, the
+// partition plan of split-context decode, and kernel launches on the caller's
+// stream.  Nothing here allocates, frees, synchronises or reads device memory.
+#include <climits>
+#include <cstdint>
+
+#include "kernels.h"
+#include "pkv.h"
+
+namespace {
+
+constexpr double kLog2e = 1.4426950408889634;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
+
+bool dtype_ok(int32_t dtype) { return dtype == PKV_BF16 || dtype == PKV_FP16; }
+
+bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 1024 && bs % 16 == 0; }
+
+// Tokens per partition for the automatic plan: the largest of 512/256/128
+// that still yields >= 2048 (sequence, kv head, partition) workgroups -- eight
+// per compute unit -- so that ragged lengths even out; 0 (one pass, no merge)
+// when the longest context fits one partition.
+int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
+  int32_t pt = 512;
+  while (pt > 128 &&
+         static_cast<int64_t>(num_seqs) * num_kv_heads * ((max_ctx + pt - 1) / pt) < 2048)
+    pt /= 2;
+  return pt >= max_ctx ? 0 : pt;
+}
+
+struct Plan {
+  int32_t part_tokens;  // multiple of 16
+  int32_t num_parts;
+};
+
+Plan make_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, int32_t partition_tokens) {
+  int32_t pt = partition_tokens > 0 ? partition_tokens : auto_partition(num_seqs, num_kv_heads, max_ctx);
+  if (pt <= 0 || pt >= max_ctx) {
+    const int32_t one = max_ctx <= 16 ? 16 : ((max_ctx + 15) / 16) * 16;
+    return {one, 1};
+  }
+  return {pt, (max_ctx + pt - 1) / pt};
+}
+
+size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, const Plan& plan) {
+  if (plan.num_parts <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * plan.num_parts;
+  return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_str(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_E_NULL: return "required pointer is NULL";
+    case PKV_E_SHAPE: return "sizes inconsistent, out of range or misaligned";
+    case PKV_E_UNSUPPORTED: return "dtype, head_dim, block_size or GQA group not supported";
+    case PKV_E_WORKSPACE: return "workspace missing or too small";
+    case PKV_E_HIP: return "HIP kernel launch failed";
+    case PKV_E_NOMEM: return "not enough free blocks";
+    case PKV_E_NOSEQ: return "unknown sequence id";
+    case PKV_E_EXISTS: return "sequence id already present";
+    default: return "unknown status";
+  }
+}
+
+int pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                  void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_E_SHAPE;
+  if (!dtype_ok(dtype) || !block_size_ok(block_size) || head_dim <= 0 || head_dim % 8 || head_dim > 512)
+    return PKV_E_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_E_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_E_SHAPE;
+  if (static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 8) > static_cast<int64_t>(INT_MAX) * 256)
+    return PKV_E_SHAPE;
+  pkv::AppendParams p;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.slot_mapping = slot_mapping;
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  return pkv::launch_kv_append(p, stream) == hipSuccess ? PKV_OK : PKV_E_HIP;
+}
+
+int pkv_decode_supported(int32_t impl, int32_t dtype, int32_t head_dim, int32_t group) {
+  if (!dtype_ok(dtype)) return 0;
+  switch (impl) {
+    case PKV_IMPL_AUTO:
+      return pkv::simt_supported(dtype, head_dim, group) || pkv::mfma_supported(dtype, head_dim, group);
+    case PKV_IMPL_SIMT: return pkv::simt_supported(dtype, head_dim, group);
+    case PKV_IMPL_MFMA: return pkv::mfma_supported(dtype, head_dim, group);
+    default: return 0;
+  }
+}
+
+int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
+                                  int32_t max_context_len) {
+  (void)block_size;
+  if (num_seqs <= 0 || num_kv_heads <= 0 || max_context_len <= 0) return 0;
+  return auto_partition(num_seqs, num_kv_heads, max_context_len);
+}
+
+size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                     int32_t partition_tokens) {
+  (void)block_size;
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    return 0;
+  const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+  return workspace_for(num_seqs, num_q_heads, head_dim, plan);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_context_len) {
+  return pkv_decode_workspace_bytes_ex(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                       max_context_len, 0);
+}
+
+int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len, float scale,
+                             void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                             int32_t impl, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      max_context_len < 0)
+    return PKV_E_SHAPE;
+  if (num_q_heads % num_kv_heads) return PKV_E_SHAPE;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PKV_E_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % 16) return PKV_E_SHAPE;
+  if (!dtype_ok(dtype) || !block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  const bool simt_ok = pkv::simt_supported(dtype, head_dim, group);
+  const bool mfma_ok = pkv::mfma_supported(dtype, head_dim, group);
+  bool use_mfma;
+  switch (impl) {
+    case PKV_IMPL_AUTO:
+      if (!simt_ok && !mfma_ok) return PKV_E_UNSUPPORTED;
+      use_mfma = mfma_ok;
+      break;
+    case PKV_IMPL_SIMT:
+      if (!simt_ok) return PKV_E_UNSUPPORTED;
+      use_mfma = false;
+      break;
+    case PKV_IMPL_MFMA:
+      if (!mfma_ok) return PKV_E_UNSUPPORTED;
+      use_mfma = true;
+      break;
+    default: return PKV_E_UNSUPPORTED;
+  }
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_E_SHAPE;
+
+  const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, plan);
+  if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return PKV_E_WORKSPACE;
+  const int64_t items = static_cast<int64_t>(num_seqs) * plan.num_parts * num_kv_heads;
+  if (items > INT_MAX) return PKV_E_SHAPE;
+
+  pkv::DecodeParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.part_o = nullptr;
+  p.part_m = nullptr;
+  p.part_l = nullptr;
+  if (need > 0) {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * plan.num_parts;
+    char* ws = static_cast<char*>(workspace);
+    p.part_o = reinterpret_cast<float*>(ws);
+    p.part_m = reinterpret_cast<float*>(ws + align256(rows * head_dim * sizeof(float)));
+    p.part_l = reinterpret_cast<float*>(ws + align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)));
+  }
+  p.num_seqs = num_seqs;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.part_tokens = plan.part_tokens;
+  p.num_parts = plan.num_parts;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+
+  hipError_t e = use_mfma ? pkv::launch_decode_mfma(p, dtype, stream) : pkv::launch_decode_simt(p, dtype, stream);
+  if (e != hipSuccess) return PKV_E_HIP;
+  if (plan.num_parts > 1) {
+    e = pkv::launch_merge(p, dtype, stream);
+    if (e != hipSuccess) return PKV_E_HIP;
+  }
+  return PKV_OK;
+}
+
+int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t max_context_len, float scale,
+                          void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return pkv_paged_attn_decode_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                  max_context_len, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  block_size, num_blocks, dtype, workspace, workspace_bytes, 0, PKV_IMPL_AUTO,
+                                  stream);
+}
+
+}  // extern "C"

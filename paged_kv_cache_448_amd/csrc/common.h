@@ -1,0 +1,60 @@
+// Device-side helpers shared by the kernels of the paged KV-cache library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kWave = 64;
+constexpr int kSubTile = 16;  // tokens per cache sub-tile
+
+struct Bf16 {};
+struct Fp16 {};
+
+// The two 16-bit values packed in w, as fp32 (exact conversions).
+template <typename T> __device__ __forceinline__ float lo_f32(uint32_t w);
+template <typename T> __device__ __forceinline__ float hi_f32(uint32_t w);
+
+template <> __device__ __forceinline__ float lo_f32<Bf16>(uint32_t w) { return __uint_as_float(w << 16); }
+template <> __device__ __forceinline__ float hi_f32<Bf16>(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <> __device__ __forceinline__ float lo_f32<Fp16>(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+template <> __device__ __forceinline__ float hi_f32<Fp16>(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// Quiet-NaN bit pattern of each storage type.
+template <typename T> inline constexpr uint16_t kNanBits = 0;
+template <> inline constexpr uint16_t kNanBits<Bf16> = 0x7fc0;
+template <> inline constexpr uint16_t kNanBits<Fp16> = 0x7e00;
+
+// fp32 -> 16-bit storage, round to nearest even.
+template <typename T> __device__ __forceinline__ uint16_t to_bits(float f);
+template <> __device__ __forceinline__ uint16_t to_bits<Bf16>(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays a quiet NaN
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+template <> __device__ __forceinline__ uint16_t to_bits<Fp16>(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (bid % 8).  Give each
+// XCD a contiguous range of work items instead, so items that touch the same
+// data (a sequence's partitions, sequences sharing prefix blocks) share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int nx = n >> 3, rem = n & 7, x = bid & 7, k = bid >> 3;
+  return x * nx + (x < rem ? x : rem) + k;
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pkv

@@ -1,0 +1,83 @@
+// Pieces shared by the decode kernels: work-item decoding, sequence checks and
+// the workgroup epilogue that folds the waves' partial softmax states together.
+//
+// Every wave keeps an online-softmax state over the tokens it saw: a running
+// maximum m (log2 units, scale folded in), a denominator l and an unnormalised
+// accumulator o = sum_t 2^(s_t - m) v_t.  States combine exactly by the
+// log-sum-exp identity: with M = max_w m_w,
+//   l = sum_w 2^(m_w - M) l_w,   o = sum_w 2^(m_w - M) o_w,   out = o / l.
+// The same identity merges the partitions of a long context in merge.hip.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace pkv {
+
+struct WorkItem {
+  int seq, kvh, part;
+};
+
+// Items are ordered (sequence, partition, kv head); see xcd_remap for the
+// workgroup -> item order.
+__device__ __forceinline__ WorkItem decode_item(const DecodeParams& p) {
+  int it = xcd_remap(blockIdx.x, gridDim.x);
+  WorkItem w;
+  w.kvh = it % p.num_kv_heads;
+  it /= p.num_kv_heads;
+  w.part = it % p.num_parts;
+  w.seq = it / p.num_parts;
+  return w;
+}
+
+// A context length the kernel must not trust: outside [0, max_context_len] or
+// beyond what the block table can hold.
+__device__ __forceinline__ bool bad_length(int L, const DecodeParams& p) {
+  return L < 0 || L > p.max_context_len ||
+         static_cast<int64_t>(L) > static_cast<int64_t>(p.max_blocks_per_seq) * p.block_size;
+}
+
+// For an empty or invalid sequence the workgroup of partition 0 writes the
+// G heads' output (zeros or NaN); the others do nothing.
+template <typename T, int G, int NT>
+__device__ __forceinline__ void write_degenerate(const DecodeParams& p, const WorkItem& w, bool bad) {
+  if (w.part != 0) return;
+  const int D = p.head_dim;
+  const uint16_t v = bad ? kNanBits<T> : 0;
+  uint16_t* o = p.out + (static_cast<size_t>(w.seq) * p.num_q_heads + w.kvh * G) * D;
+  for (int i = threadIdx.x; i < G * D; i += NT) o[i] = v;
+}
+
+// Fold NW waves' states (in LDS) and store either the final output (the whole
+// context was one partition) or this partition's partial state.
+template <typename T, int D, int G, int NW>
+__device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const float (*sm_l)[G],
+                                                  const float (*sm_o)[G][D], const DecodeParams& p,
+                                                  const WorkItem& w, bool single) {
+  for (int i = threadIdx.x; i < G * D; i += NW * kWave) {
+    const int h = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, sm_m[k][h]);
+    float lt = 0.f, o = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const float c = fast_exp2(sm_m[k][h] - M);
+      lt = fmaf(c, sm_l[k][h], lt);
+      o = fmaf(c, sm_o[k][h][d], o);
+    }
+    const size_t row = static_cast<size_t>(w.seq) * p.num_q_heads + w.kvh * G + h;
+    if (single) {
+      p.out[row * D + d] = to_bits<T>(o / lt);
+    } else {
+      const size_t pr = row * p.num_parts + w.part;
+      p.part_o[pr * D + d] = o;
+      if (d == 0) {
+        p.part_m[pr] = M;
+        p.part_l[pr] = lt;
+      }
+    }
+  }
+}
+
+}  // namespace pkv

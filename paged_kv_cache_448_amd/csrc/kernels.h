@@ -1,0 +1,46 @@
+// Kernel parameter blocks and launchers (internal to the library; the public
+// interface is include/pkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendParams {
+  const uint16_t* k;            // [T, Hkv, D]
+  const uint16_t* v;            // [T, Hkv, D]
+  const int64_t* slot_mapping;  // [T]
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t num_tokens, num_blocks, block_size, num_kv_heads, head_dim;
+};
+
+struct DecodeParams {
+  const uint16_t* q;             // [B, Hq, D]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;   // [B, max_blocks_per_seq]
+  const int32_t* context_lens;   // [B]
+  uint16_t* out;                 // [B, Hq, D]
+  float* part_o;                 // [B, Hq, num_parts, D]  (only when num_parts > 1)
+  float* part_m;                 // [B, Hq, num_parts]     running max, log2 units
+  float* part_l;                 // [B, Hq, num_parts]     softmax denominator
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  int32_t max_blocks_per_seq, max_context_len;
+  int32_t part_tokens;           // tokens per partition, a multiple of 16
+  int32_t num_parts;             // ceil(max_context_len / part_tokens), >= 1
+  float scale_log2;              // softmax scale * log2(e)
+};
+
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
+
+bool simt_supported(int dtype, int head_dim, int group);
+hipError_t launch_decode_simt(const DecodeParams& p, int dtype, hipStream_t stream);
+
+bool mfma_supported(int dtype, int head_dim, int group);
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, hipStream_t stream);
+
+hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,55 @@
+// Merge pass of split-context decode: combine the per-partition softmax
+// states of a sequence into its output with the log-sum-exp identity
+// (see decode_common.h).  One wave per (sequence, q head); lane l owns dims
+// l and l+64.  Partitions are folded in index order, so the result does not
+// depend on which workgroup finished first.
+//
+// The pages never split a context; this pass exists because on one GPU a few
+// long sequences alone cannot fill 256 compute units.
+#include "decode_common.h"
+
+namespace pkv {
+
+namespace {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
+  constexpr int DV = D / 64;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;  // seq * Hq + q head
+  if (row >= p.num_seqs * p.num_q_heads) return;
+  const int seq = row / p.num_q_heads;
+  const int L = p.context_lens[seq];
+  if (bad_length(L, p) || L <= p.part_tokens) return;  // written by the partition kernel
+  const int np = (L + p.part_tokens - 1) / p.part_tokens;
+  const size_t base = static_cast<size_t>(row) * p.num_parts;
+  float M = -INFINITY;
+  for (int i = 0; i < np; ++i) M = fmaxf(M, p.part_m[base + i]);
+  float lt = 0.f, o[DV];
+#pragma unroll
+  for (int e = 0; e < DV; ++e) o[e] = 0.f;
+  for (int i = 0; i < np; ++i) {
+    const float c = fast_exp2(p.part_m[base + i] - M);
+    lt = fmaf(c, p.part_l[base + i], lt);
+#pragma unroll
+    for (int e = 0; e < DV; ++e) o[e] = fmaf(c, p.part_o[(base + i) * D + lane + 64 * e], o[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < DV; ++e) p.out[static_cast<size_t>(row) * D + lane + 64 * e] = to_bits<T>(o[e] / lt);
+}
+
+template <typename T, int D>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(p.num_seqs) * p.num_q_heads;
+  hipLaunchKernelGGL((merge_kernel<T, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream) {
+  if (dtype == 0) return p.head_dim == 64 ? launch_t<Bf16, 64>(p, stream) : launch_t<Bf16, 128>(p, stream);
+  return p.head_dim == 64 ? launch_t<Fp16, 64>(p, stream) : launch_t<Fp16, 128>(p, stream);
+}
+
+}  // namespace pkv

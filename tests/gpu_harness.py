@@ -1,0 +1,125 @@
+"""Moving seeded workloads to the GPU and comparing the HIP path with the oracle.
+
+The GPU side only ever goes through the C-ABI library (via the package's ctypes
+binding); the oracle side only through ``oracle``.  Both start from the same
+generator arrays; tail slots are poisoned with NaN by each side's own append.
+"""
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_448_amd as pkv
+import workloads
+from oracle.numerics import bits_to_f64
+
+TORCH_DTYPE = {"bf16": torch.bfloat16, "fp16": torch.float16}
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+def to_dev(a, dtype, shape=None):
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(TORCH_DTYPE[dtype])
+    if shape is not None:
+        t = t.reshape(shape)
+    return t.cuda()
+
+
+def to_bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+@dataclasses.dataclass
+class DevLayer:
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+
+
+@dataclasses.dataclass
+class DevWorkload:
+    tables: torch.Tensor
+    lens: torch.Tensor
+    slots: torch.Tensor
+    layers: list
+
+
+def cache_shape(wl):
+    c = wl.cfg
+    return (wl.num_blocks, c.num_kv_heads, c.block_size // 16, 16 * c.head_dim)
+
+
+def upload(wl, layers=None):
+    c = wl.cfg
+    idx = range(len(wl.layers)) if layers is None else layers
+    dl = []
+    for i in idx:
+        ly = wl.layers[i]
+        dl.append(DevLayer(to_dev(ly.q, c.dtype), to_dev(ly.k_cache, c.dtype, cache_shape(wl)),
+                           to_dev(ly.v_cache, c.dtype, cache_shape(wl)), to_dev(ly.k_new, c.dtype),
+                           to_dev(ly.v_new, c.dtype)))
+    return DevWorkload(torch.from_numpy(wl.block_tables).cuda(), torch.from_numpy(wl.context_lens).cuda(),
+                       torch.from_numpy(wl.slot_mapping).cuda(), dl)
+
+
+def poison_tails_gpu(wl, dev_layer):
+    if len(wl.tail_slots) == 0:
+        return
+    nan = to_dev(workloads.nan_tokens(len(wl.tail_slots), wl.cfg), wl.cfg.dtype)
+    pkv.kv_append(nan, nan, torch.from_numpy(wl.tail_slots).cuda(), dev_layer.k_cache, dev_layer.v_cache)
+
+
+def poison_tails_oracle(wl, kc, vc):
+    if len(wl.tail_slots) == 0:
+        return
+    nan = workloads.nan_tokens(len(wl.tail_slots), wl.cfg)
+    oracle.kv_append(nan, nan, wl.tail_slots, kc, vc, num_blocks=wl.num_blocks, block_size=wl.cfg.block_size)
+
+
+def oracle_caches(wl, layer_idx, append=True):
+    """Host caches after tail poisoning and (optionally) this step's append."""
+    ly = wl.layers[layer_idx]
+    kc, vc = ly.k_cache.copy(), ly.v_cache.copy()
+    poison_tails_oracle(wl, kc, vc)
+    if append:
+        oracle.kv_append(ly.k_new, ly.v_new, wl.slot_mapping, kc, vc, num_blocks=wl.num_blocks,
+                         block_size=wl.cfg.block_size)
+    return kc, vc
+
+
+def oracle_decode(wl, layer_idx, kc, vc, seqs=None, scale=None, lens=None, tables=None):
+    c = wl.cfg
+    return oracle.decode(wl.layers[layer_idx].q, kc, vc, wl.block_tables if tables is None else tables,
+                         wl.context_lens if lens is None else lens, c.scale if scale is None else scale,
+                         dtype=c.dtype, num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads,
+                         block_size=c.block_size, seqs=seqs)
+
+
+def gpu_decode(wl, dw, dev_layer, impl="auto", partition_tokens=0, scale=None, lens=None, tables=None,
+               max_context_len=None):
+    c = wl.cfg
+    L = dw.lens if lens is None else lens
+    mcl = int(wl.context_lens.max()) if max_context_len is None else max_context_len
+    out = pkv.paged_attn_decode(dev_layer.q, dev_layer.k_cache, dev_layer.v_cache,
+                                dw.tables if tables is None else tables, L,
+                                c.scale if scale is None else scale, max_context_len=max(mcl, 0),
+                                partition_tokens=partition_tokens, impl=impl)
+    return out
+
+
+def parity_error(out_bits, ref, dtype):
+    """Max of |gpu - ref| / (ATOL + RTOL |ref|); <= 1 passes."""
+    got = bits_to_f64(out_bits, dtype)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{np.count_nonzero(~np.isfinite(got))} non-finite outputs"
+    err = np.abs(got - ref)
+    return float((err / (ATOL + RTOL * np.abs(ref))).max()), float(err.max())
+
+
+def assert_parity(out_bits, ref, dtype, what=""):
+    ratio, maxerr = parity_error(out_bits, ref, dtype)
+    assert ratio <= 1.0, f"{what}: max |err| {maxerr:.3e}, ratio to tolerance {ratio:.3f}"
+    return ratio, maxerr

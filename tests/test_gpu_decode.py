@@ -1,0 +1,203 @@
+"""paged_attn_decode on the GPU against the fp64 oracle, plus the invariants and
+edge cases that pin it independently of the oracle.
+
+Tolerance: |gpu - oracle| <= 1e-2 + 1e-2 |oracle| elementwise, no NaN/Inf.
+"""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_448_amd as pkv
+import workloads
+from gpu_harness import assert_parity, gpu_decode, oracle_caches, oracle_decode, poison_tails_gpu, to_bits, upload
+from oracle.numerics import bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def impls_for(cfg):
+    return [i for i in ("simt", "mfma") if pkv.decode_supported(i, cfg.dtype, cfg.head_dim, cfg.group)]
+
+
+@functools.lru_cache(maxsize=1)
+def _wl(cid):
+    return workloads.build(cid)
+
+
+@functools.lru_cache(maxsize=4)
+def _prepared(cid, layer):
+    """Oracle caches (poisoned, appended) and the oracle output for one layer."""
+    wl = _wl(cid)
+    kc, vc = oracle_caches(wl, layer)
+    return kc, vc, oracle_decode(wl, layer, kc, vc)
+
+
+def _dev_layer(wl, layer):
+    dw = upload(wl, layers=[layer])
+    d = dw.layers[0]
+    poison_tails_gpu(wl, d)
+    pkv.kv_append(d.k_new, d.v_new, dw.slots, d.k_cache, d.v_cache)
+    return dw, d
+
+
+# partition choices: automatic, one pass, and forced splits of several sizes
+PARTS = {1: [0, 16, 32], 2: [0, 4096, 128, 512], 3: [0, 8192, 256, 1024], 4: [0, 4096, 512], 5: [0, 8192, 256]}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_decode_parity(cid):
+    wl = _wl(cid)
+    kc, vc, ref = _prepared(cid, 0)
+    dw, d = _dev_layer(wl, 0)
+    for impl in impls_for(wl.cfg):
+        for pt in PARTS[cid]:
+            out = gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt)
+            r, e = assert_parity(to_bits(out), ref, wl.cfg.dtype, f"config {cid} impl {impl} partition {pt}")
+            print(f"config {cid} impl {impl} partition {pt}: max|err| {e:.2e} (ratio {r:.3f})", flush=True)
+
+
+def test_decode_parity_cb_step_all_layers():
+    """Config 5: 16 layers, each an append of one token per sequence then decode,
+    every sequence of every layer compared with the oracle."""
+    wl = _wl(5)
+    worst = 0.0
+    for li in range(len(wl.layers)):
+        dw, d = _dev_layer(wl, li)
+        kc, vc = oracle_caches(wl, li)
+        ref = oracle_decode(wl, li, kc, vc)
+        for impl in impls_for(wl.cfg):
+            out = gpu_decode(wl, dw, d, impl=impl)
+            r, e = assert_parity(to_bits(out), ref, wl.cfg.dtype, f"config 5 layer {li} impl {impl}")
+            worst = max(worst, r)
+        del dw, d
+    print(f"config 5: worst ratio to tolerance {worst:.3f}", flush=True)
+
+
+def _agree(a_bits, b_bits, dtype):
+    """Two GPU results that differ only by fp32 summation order: within one unit of
+    the 16-bit format relative to the value, plus 1e-5 absolute for outputs near 0."""
+    a, b = bits_to_f64(a_bits, dtype), bits_to_f64(b_bits, dtype)
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
+    return float((np.abs(a - b) / (1e-5 + ulp * np.abs(b))).max())
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_split_and_single_pass_agree(cid):
+    """Log-sum-exp merge of partitions vs one pass: equal up to fp32 summation order."""
+    wl = _wl(cid)
+    dw, d = _dev_layer(wl, 0)
+    for impl in impls_for(wl.cfg):
+        single = to_bits(gpu_decode(wl, dw, d, impl=impl, partition_tokens=1 << 14))
+        for pt in (128, 256, 512):
+            split = to_bits(gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt))
+            assert _agree(split, single, wl.cfg.dtype) <= 1.0, f"impl {impl} partition {pt}"
+
+
+@pytest.mark.parametrize("cid", [1, 2, 4])
+def test_deterministic(cid):
+    wl = _wl(cid)
+    dw, d = _dev_layer(wl, 0)
+    for impl in impls_for(wl.cfg):
+        a = to_bits(gpu_decode(wl, dw, d, impl=impl))
+        b = to_bits(gpu_decode(wl, dw, d, impl=impl))
+        assert np.array_equal(a, b)
+
+
+def test_impls_agree():
+    wl = _wl(2)
+    dw, d = _dev_layer(wl, 0)
+    impls = impls_for(wl.cfg)
+    outs = [to_bits(gpu_decode(wl, dw, d, impl=i)) for i in impls]
+    for o in outs[1:]:
+        assert _agree(o, outs[0], wl.cfg.dtype) <= 1.0
+
+
+def _custom(Hq, Hkv, D, bs, lens, dtype="bf16", seed=0):
+    wl = workloads.custom(Hq, Hkv, D, bs, lens, dtype, seed=seed, spare_blocks=2)
+    kc, vc = oracle_caches(wl, 0)
+    dw, d = _dev_layer(wl, 0)
+    return wl, kc, vc, dw, d
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype", [
+    (4, 2, 64, 16, "bf16"), (8, 1, 64, 32, "bf16"), (16, 16, 64, 16, "fp16"), (8, 4, 128, 64, "bf16"),
+    (2, 1, 128, 256, "fp16"), (16, 2, 64, 128, "bf16"), (32, 2, 64, 16, "bf16"), (16, 1, 128, 16, "fp16")])
+def test_ragged_lengths_and_shapes(Hq, Hkv, D, bs, dtype):
+    """Lengths around sub-tile and block edges, several tiles and a ragged tail."""
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 100, 255, 256, 257, 700, 1023]
+    wl, kc, vc, dw, d = _custom(Hq, Hkv, D, bs, lens, dtype, seed=Hq + D + bs)
+    ref = oracle_decode(wl, 0, kc, vc)
+    impls = [i for i in ("simt", "mfma") if pkv.decode_supported(i, dtype, D, Hq // Hkv)]
+    if not impls:
+        pytest.skip(f"no decode kernel built for G={Hq // Hkv}, D={D}")
+    for impl in impls:
+        for pt in (0, 16, 64, 256, 4096):
+            out = gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt)
+            assert_parity(to_bits(out), ref, dtype, f"impl {impl} partition {pt}")
+
+
+def test_length_one_is_exactly_v0():
+    lens = [1] * 9
+    wl, kc, vc, dw, d = _custom(8, 2, 64, 16, lens, seed=3)
+    G = 4
+    v0 = wl.layers[0].v_new  # the appended token is the whole context
+    for impl in impls_for(wl.cfg):
+        out = to_bits(gpu_decode(wl, dw, d, impl=impl))
+        for h in range(8):
+            assert np.array_equal(out[:, h, :], v0[:, h // G, :]), impl
+
+
+def test_block_permutation_gives_identical_output():
+    wl = _wl(2)
+    dw, d = _dev_layer(wl, 0)
+    N = wl.num_blocks
+    perm = torch.from_numpy(np.random.default_rng(5).permutation(N)).cuda()
+    kp = torch.empty_like(d.k_cache)
+    vp = torch.empty_like(d.v_cache)
+    kp[perm] = d.k_cache
+    vp[perm] = d.v_cache
+    tables = perm[dw.tables.long()].to(torch.int32).contiguous()
+    for impl in impls_for(wl.cfg):
+        a = to_bits(gpu_decode(wl, dw, d, impl=impl))
+        moved = type(d)(d.q, kp, vp, d.k_new, d.v_new)
+        b = to_bits(gpu_decode(wl, dw, moved, impl=impl, tables=tables))
+        assert np.array_equal(a, b), impl
+
+
+def test_empty_and_invalid_sequences():
+    """L=0 gives zeros; L above max_context_len, or a block id outside the pool,
+    gives NaN for that sequence only -- and nothing is read outside the pool."""
+    lens = [0, 40, 40, 40, 17]
+    wl, kc, vc, dw, d = _custom(4, 2, 64, 16, lens, seed=9)
+    ref = oracle_decode(wl, 0, kc, vc)
+    L = dw.lens.clone()
+    L[2] = 41  # above max_context_len passed below
+    tables = dw.tables.clone()
+    tables[3, 1] = wl.num_blocks + 5
+    tables[4, 0] = -3
+    for impl in impls_for(wl.cfg):
+        for pt in (0, 16):
+            out = gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt, lens=L, tables=tables, max_context_len=40)
+            got = bits_to_f64(to_bits(out), "bf16")
+            assert np.array_equal(got[0], np.zeros_like(got[0]))
+            assert_parity(to_bits(out)[1:2], ref[1:2], "bf16", impl)
+            for i in (2, 3, 4):
+                assert np.isnan(got[i]).all(), (impl, pt, i)
+
+
+def test_scale_zero_is_mean_of_v():
+    lens = [5, 37, 64]
+    wl, kc, vc, dw, d = _custom(4, 2, 64, 16, lens, seed=4)
+    ref = oracle_decode(wl, 0, kc, vc, scale=0.0)
+    for impl in impls_for(wl.cfg):
+        assert_parity(to_bits(gpu_decode(wl, dw, d, impl=impl, scale=0.0)), ref, "bf16", impl)
+
+
+def test_empty_batch_is_a_no_op():
+    wl = _wl(1)
+    dw, d = _dev_layer(wl, 0)
+    q = d.q[:0]
+    out = pkv.paged_attn_decode(q, d.k_cache, d.v_cache, dw.tables[:0], dw.lens[:0], 0.125, max_context_len=0)
+    assert out.shape[0] == 0
