@@ -75,12 +75,20 @@ def test_decode_parity_cb_step_all_layers():
     print(f"config 5: worst ratio to tolerance {worst:.3f}", flush=True)
 
 
-def _agree(a_bits, b_bits, dtype):
-    """Two GPU results that differ only by fp32 summation order: within one unit of
-    the 16-bit format relative to the value, plus 1e-5 absolute for outputs near 0."""
+def _agree(a_bits, b_bits, dtype, p_rounded):
+    """Ratio of |a - b| to the bound for two GPU results of the same inputs.
+
+    Both are rounded to the 16-bit output type (one unit relative).  The SIMT
+    kernel differs between plans only by fp32 summation order (1e-5 absolute).
+    The MFMA kernel also rounds each probability to the 16-bit type (relative
+    error u = 2^-9 bf16 / 2^-12 fp16) against a running maximum that depends on
+    the plan, so two plans' outputs may differ by up to 2u * sum_t w_t |v_t - out|;
+    with N(0,1) values that weighted deviation stays below 4, giving 8u absolute."""
     a, b = bits_to_f64(a_bits, dtype), bits_to_f64(b_bits, dtype)
     ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
-    return float((np.abs(a - b) / (1e-5 + ulp * np.abs(b))).max())
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -12
+    atol = 8 * u if p_rounded else 1e-5
+    return float((np.abs(a - b) / (atol + ulp * np.abs(b))).max())
 
 
 @pytest.mark.parametrize("cid", [2, 3])
@@ -92,7 +100,9 @@ def test_split_and_single_pass_agree(cid):
         single = to_bits(gpu_decode(wl, dw, d, impl=impl, partition_tokens=1 << 14))
         for pt in (128, 256, 512):
             split = to_bits(gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt))
-            assert _agree(split, single, wl.cfg.dtype) <= 1.0, f"impl {impl} partition {pt}"
+            r = _agree(split, single, wl.cfg.dtype, impl == "mfma")
+            print(f"config {cid} impl {impl} partition {pt}: ratio to bound {r:.3f}", flush=True)
+            assert r <= 1.0, f"impl {impl} partition {pt}"
 
 
 @pytest.mark.parametrize("cid", [1, 2, 4])
@@ -111,7 +121,9 @@ def test_impls_agree():
     impls = impls_for(wl.cfg)
     outs = [to_bits(gpu_decode(wl, dw, d, impl=i)) for i in impls]
     for o in outs[1:]:
-        assert _agree(o, outs[0], wl.cfg.dtype) <= 1.0
+        r = _agree(o, outs[0], wl.cfg.dtype, True)
+        print(f"impls agree: ratio to bound {r:.3f}", flush=True)
+        assert r <= 1.0
 
 
 def _custom(Hq, Hkv, D, bs, lens, dtype="bf16", seed=0):
