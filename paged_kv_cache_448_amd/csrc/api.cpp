@@ -19,15 +19,21 @@ bool dtype_ok(int32_t dtype) { return dtype == PKV_BF16 || dtype == PKV_FP16; }
 
 bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 1024 && bs % 16 == 0; }
 
-// Tokens per partition for the automatic plan: the largest of 512/256/128
-// that still yields >= 2048 (sequence, kv head, partition) workgroups -- eight
-// per compute unit -- so that ragged lengths even out; 0 (one pass, no merge)
-// when the longest context fits one partition.
+// Compute units the automatic plan is sized for (MI355X).
+constexpr int64_t kPlanCUs = 256;
+
+// Tokens per partition for the automatic plan, 0 for one pass without merge.
+// One workgroup per (sequence, kv head) reads a whole context when there are
+// at least two such units per compute unit and no context is longer than
+// 4096 tokens: on the ragged Llama-3.2-1B batch this is faster than any split
+// plus the merge pass.  Otherwise contexts are cut into partitions of
+// 2048 tokens or fewer (power of two, down to 256) so that there are at least
+// two (sequence, kv head, partition) workgroups per compute unit.
 int32_t auto_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx) {
-  int32_t pt = 512;
-  while (pt > 128 &&
-         static_cast<int64_t>(num_seqs) * num_kv_heads * ((max_ctx + pt - 1) / pt) < 2048)
-    pt /= 2;
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  if (units >= 2 * kPlanCUs && max_ctx <= 4096) return 0;
+  int32_t pt = 2048;
+  while (pt > 256 && units * ((max_ctx + pt - 1) / pt) < 2 * kPlanCUs) pt /= 2;
   return pt >= max_ctx ? 0 : pt;
 }
 
@@ -38,11 +44,11 @@ struct Plan {
 
 Plan make_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, int32_t partition_tokens) {
   int32_t pt = partition_tokens > 0 ? partition_tokens : auto_partition(num_seqs, num_kv_heads, max_ctx);
-  if (pt <= 0 || pt >= max_ctx) {
-    const int32_t one = max_ctx <= 16 ? 16 : ((max_ctx + 15) / 16) * 16;
-    return {one, 1};
-  }
-  return {pt, (max_ctx + pt - 1) / pt};
+  if (pt <= 0 || pt >= max_ctx) pt = max_ctx <= 16 ? 16 : ((max_ctx + 15) / 16) * 16;
+  // a workgroup of the MFMA kernel takes at most kMaxPartitionTokens tokens
+  if (pt > pkv::kMaxPartitionTokens) pt = pkv::kMaxPartitionTokens;
+  const int32_t parts = max_ctx <= pt ? 1 : (max_ctx + pt - 1) / pt;
+  return {pt, parts};
 }
 
 size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, const Plan& plan) {
@@ -110,7 +116,8 @@ int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_
                                   int32_t max_context_len) {
   (void)block_size;
   if (num_seqs <= 0 || num_kv_heads <= 0 || max_context_len <= 0) return 0;
-  return auto_partition(num_seqs, num_kv_heads, max_context_len);
+  const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, 0);
+  return plan.num_parts > 1 ? plan.part_tokens : 0;
 }
 
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

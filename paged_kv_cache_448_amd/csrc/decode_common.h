@@ -80,4 +80,24 @@ __device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const 
   }
 }
 
+// Output element (row = sequence * Hq + q head, dim d) of a split context,
+// folded from the first nparts partition states of that row in index order
+// with the log-sum-exp identity, as a running (M, l, o) so that all loads of a
+// row can be in flight together.
+template <int D>
+__device__ __forceinline__ float merge_row_elem(const DecodeParams& p, size_t row, int d, int nparts) {
+  const size_t base = row * p.num_parts;
+  float M = -INFINITY, lt = 0.f, o = 0.f;
+#pragma unroll 4
+  for (int k = 0; k < nparts; ++k) {
+    const float mk = p.part_m[base + k], lk = p.part_l[base + k], ok = p.part_o[(base + k) * D + d];
+    const float mn = fmaxf(M, mk);
+    const float a = fast_exp2(M - mn), b = fast_exp2(mk - mn);
+    lt = fmaf(lt, a, lk * b);
+    o = fmaf(o, a, ok * b);
+    M = mn;
+  }
+  return o / lt;
+}
+
 }  // namespace pkv

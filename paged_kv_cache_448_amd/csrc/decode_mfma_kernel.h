@@ -1,0 +1,240 @@
+// Paged decode attention on the matrix cores (MFMA) of gfx950: the kernel
+// template.  decode_mfma.hip instantiates it and launches it.
+//
+// Same result as the vector-ALU kernel -- softmax(scale q K^T) V over each
+// sequence's paged context with GQA ("[Hacker News 요약] C++와 CUDA로 vLLM의 경량
+// 고성능 LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section "고성능 추론을 위한 고급
+// 최적화 기법"; paging per "vLLM -- PagedAttention으로 LLM 추론 성능을 2~4배
+// 끌어올린 서빙 엔진", section "PagedAttention -- OS 가상 메모리에서 영감") -- but the
+// two contractions of a 16-token sub-tile run as MFMA tiles, so the vector ALU
+// only does the softmax:
+//
+//   S^T[16 tok x 16 cols] = K[16 tok x D] . Q^T[D x 16 cols]   (D/32 x mfma 16x16x32)
+//   O^T[D x 16 cols]     += V^T[D x 16 tok] . P^T[16 tok x 16 cols] (D/16 x mfma 16x16x16)
+//
+// The 16 columns are the G q heads that share the kv head (G <= 16; unused
+// columns hold zero queries).  The cache layout makes every operand a plain
+// coalesced load: lane l = 16*kg + r reads the 16-byte K run kg (+4j) of token
+// r -- for fixed j the wave reads one contiguous KB -- and the 8-byte V piece
+// (dim 16j + r, tokens 4kg..4kg+3) -- 512 contiguous bytes per j.  The S tile
+// comes back with lane l holding tokens 4kg..4kg+3 of column r, which is
+// exactly the P^T operand layout of the PV product, so probabilities never
+// leave registers.
+//
+// Softmax is online in fp32 (log2 domain).  P enters the PV product rounded to
+// the cache's 16-bit type (round to nearest even); the denominator sums the same
+// rounded values, so the output is an exact convex combination of V rows up to
+// fp32 rounding.  Tokens past the context are masked by select (score -inf, V
+// 0), so NaN in tail slots never reaches the output.
+//
+// Work split: one workgroup per (sequence, kv head, partition); its NW waves
+// take the partition's 16-token sub-tiles round robin (wave w: w, w+NW, ...).
+// Decode moves every cached byte once and does little arithmetic on it, so the
+// kernel is organised around keeping HBM busy: each wave keeps S sub-tiles
+// (S * 4 KB at D = 64) in flight, refilling a register slot as soon as its
+// sub-tile has been consumed, and every wave fetches the physical ids of all
+// its sub-tiles with one load at the start (one id per lane, read back with
+// readlane), so the only dependent HBM round trip is the block-table read.
+//
+// Partitions of one (sequence, kv head) store their softmax states and the
+// merge kernel (merge.hip) folds them.
+#pragma once
+
+#include "decode_common.h"
+
+namespace pkv {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T> struct Mma;
+
+template <> struct Mma<Bf16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  typedef short x4 __attribute__((ext_vector_type(4)));
+  typedef __bf16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0,
+                                                     0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, x2));
+  }
+};
+
+template <> struct Mma<Fp16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 x4 __attribute__((ext_vector_type(4)));
+  typedef _Float16 x2 __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ f32x4 qk(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(x4, a), __builtin_bit_cast(x4, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, x2));
+  }
+};
+
+// The registers one sub-tile needs: K operands (one per 32 dims) and V
+// operands (one per 16 dims).
+template <int D> struct Tile {
+  u32x4 k[D / 32];
+  u32x2 v[D / 16];
+};
+
+template <typename T, int D, int G, int NW, int S>
+__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p) {
+  constexpr int JK = D / 32, JV = D / 16;
+  __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
+
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int r = lane & 15, kg = lane >> 4;
+  const WorkItem w = decode_item(p);
+  const int L = p.context_lens[w.seq];
+  const bool bad_len = bad_length(L, p);
+  if (bad_len || L == 0) {
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len);
+    return;
+  }
+  const int start = w.part * p.part_tokens;
+  if (start >= L) return;
+  const int end = min(L, start + p.part_tokens);
+  const int nsub = (end - start + 15) >> 4;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  // this wave owns sub-tiles wv + k*NW, k = 0 .. n_w-1
+  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
+
+  // Q^T operand: column r = q head kvh*G + r (zero for r >= G), dims of run kg + 4j
+  u32x4 qop[JK];
+#pragma unroll
+  for (int j = 0; j < JK; ++j) {
+    if (r < G) {
+      qop[j] = *reinterpret_cast<const u32x4*>(
+          p.q + (static_cast<size_t>(w.seq) * p.num_q_heads + w.kvh * G + r) * D + (kg + 4 * j) * 8);
+    } else {
+      qop[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // lane k: index of this wave's k-th sub-tile in the pool (sub-tiles of 16*D
+  // elements, numbered (block*Hkv + kvh)*(bs/16) + sub-tile in block), or -1
+  // when the table names a block outside the pool.
+  int tid = 0;
+  if (lane < n_w) {
+    const int tok0 = start + 16 * (wv + lane * NW);
+    const int blk = tok0 / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
+    tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
+              ? (phys * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
+              : -1;
+  }
+  bool bad = false;
+
+  // Branch-free, so that every path issues the same loads and the compiler's
+  // wait counts keep S-1 sub-tiles in flight.  A bad block id makes the
+  // whole head group NaN, so what is read in its place (sub-tile 0 of the
+  // pool, always in bounds) does not matter.
+  auto load = [&](int k, Tile<D>& t) {
+    int sub = __builtin_amdgcn_readlane(tid, k);
+    bad |= sub < 0;
+    sub = max(sub, 0);
+    const uint16_t* kt = p.k_cache + static_cast<size_t>(sub) * (16 * D);
+    const uint16_t* vt = p.v_cache + static_cast<size_t>(sub) * (16 * D);
+#pragma unroll
+    for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(kt + ((4 * j + kg) * 16 + r) * 8);
+#pragma unroll
+    for (int j = 0; j < JV; ++j) t.v[j] = *reinterpret_cast<const u32x2*>(vt + (16 * j + r) * 16 + 4 * kg);
+  };
+
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[JV];
+#pragma unroll
+  for (int j = 0; j < JV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // k-th sub-tile of this wave; k >= n_w is an empty pad step (every token
+  // masked), which leaves the state unchanged since k = 0 is never empty.
+  auto compute = [&](int k, Tile<D>& t) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[j], sc);
+    const int nvalid = k < n_w ? min(16, end - (start + 16 * (wv + k * NW))) : 0;
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = 4 * kg + i < nvalid ? sc[i] * p.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    bm = fmaxf(bm, shfl_xor(bm, 16));
+    bm = fmaxf(bm, shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float al = fast_exp2(m - mn);
+    m = mn;
+    const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
+    const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
+    l = l * al + ((lo_f32<T>(p01) + hi_f32<T>(p01)) + (lo_f32<T>(p23) + hi_f32<T>(p23)));
+    if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+      for (int j = 0; j < JV; ++j) o[j] *= al;
+    }
+    if (nvalid < 16) {
+      const uint32_t m0 = (4 * kg < nvalid ? 0xffffu : 0u) | (4 * kg + 1 < nvalid ? 0xffff0000u : 0u);
+      const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < JV; ++j) {
+        t.v[j].x &= m0;
+        t.v[j].y &= m1;
+      }
+    }
+    const u32x2 pop = {p01, p23};
+#pragma unroll
+    for (int j = 0; j < JV; ++j) o[j] = Mma<T>::pv(t.v[j], pop, o[j]);
+  };
+
+  if (n_w > 0) {
+    // S register slots; slot i holds sub-tiles i, i+S, i+2S, ...  Steps past
+    // n_w re-load the wave's last sub-tile (a cache hit) and compute it as an
+    // empty pad step, so the loop body is the same straight-line code every
+    // time and the compiler's wait counts stay S-1 sub-tiles deep.
+    Tile<D> t[S];
+    const int last = n_w - 1;
+#pragma unroll
+    for (int i = 0; i < S; ++i) load(min(i, last), t[i]);
+    const int n_pad = (n_w + S - 1) / S * S;
+    int kb = 0;
+    for (; kb + S < n_pad; kb += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        compute(kb + i, t[i]);
+        load(min(kb + i + S, last), t[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S; ++i) compute(kb + i, t[i]);
+  }
+
+  // fold the four token rows (kg) of the denominator
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (bad) l = __int_as_float(0x7fc00000);
+  if (r < G) {
+    if (kg == 0) {
+      sm_m[wv][r] = m;
+      sm_l[wv][r] = l;
+    }
+#pragma unroll
+    for (int j = 0; j < JV; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm_o[wv][r][16 * j + 4 * kg + i] = o[j][i];
+  }
+  __syncthreads();
+  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1);
+}
+
+}  // namespace pkv

@@ -33,6 +33,13 @@ struct DecodeParams {
   float scale_log2;              // softmax scale * log2(e)
 };
 
+// Most tokens one decode workgroup takes (both kernels); longer contexts are
+// always split.  The MFMA kernel's waves hold the pool index of each of their
+// 16-token sub-tiles in one lane each: 8 waves x 64 lanes x 16 tokens.
+constexpr int32_t kMaxPartitionTokens = 8192;
+// Partitions longer than this run with 8 waves per workgroup, shorter ones with 4.
+constexpr int32_t kFourWaveMaxTokens = 4096;
+
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 
 bool simt_supported(int dtype, int head_dim, int group);

@@ -22,20 +22,9 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   const int L = p.context_lens[seq];
   if (bad_length(L, p) || L <= p.part_tokens) return;  // written by the partition kernel
   const int np = (L + p.part_tokens - 1) / p.part_tokens;
-  const size_t base = static_cast<size_t>(row) * p.num_parts;
-  float M = -INFINITY;
-  for (int i = 0; i < np; ++i) M = fmaxf(M, p.part_m[base + i]);
-  float lt = 0.f, o[DV];
 #pragma unroll
-  for (int e = 0; e < DV; ++e) o[e] = 0.f;
-  for (int i = 0; i < np; ++i) {
-    const float c = fast_exp2(p.part_m[base + i] - M);
-    lt = fmaf(c, p.part_l[base + i], lt);
-#pragma unroll
-    for (int e = 0; e < DV; ++e) o[e] = fmaf(c, p.part_o[(base + i) * D + lane + 64 * e], o[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < DV; ++e) p.out[static_cast<size_t>(row) * D + lane + 64 * e] = to_bits<T>(o[e] / lt);
+  for (int e = 0; e < DV; ++e)
+    p.out[static_cast<size_t>(row) * D + lane + 64 * e] = to_bits<T>(merge_row_elem<D>(p, row, lane + 64 * e, np));
 }
 
 template <typename T, int D>

@@ -84,13 +84,20 @@ def test_append_rejects_bad_arguments_before_launch(kw, status):
 
 
 def test_workspace_and_plan():
-    # configuration 2's shape: 64 sequences x 8 kv heads with contexts up to 2048
-    pt = pkv.plan_partition(64, 8, 16, 2048)
-    assert pt in (128, 256, 512)
-    parts = -(-2048 // pt)
-    assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048) >= 64 * 32 * parts * (64 + 2) * 4
+    # the Llama-3.2-1B batch shape: 64 sequences x 8 kv heads, contexts up to 2048 -> one pass, no workspace
+    assert pkv.plan_partition(64, 8, 16, 2048) == 0
+    assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048) == 0
+    # the long-context shape: 16 x 8 units cannot fill 256 compute units -> 2048-token partitions
+    pt = pkv.plan_partition(16, 8, 256, 8192)
+    assert pt == 2048
+    assert pkv.decode_workspace_bytes(16, 32, 8, 64, 256, 8192) >= 16 * 32 * 4 * (64 + 2) * 4
+    # a forced split sizes the workspace for its partitions
+    assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048, partition_tokens=512) >= 64 * 32 * 4 * (64 + 2) * 4
     # a context that fits one partition needs no workspace
     assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048, partition_tokens=4096) == 0
     assert pkv.decode_workspace_bytes(2, 4, 2, 64, 16, 37) == 0
+    # partitions never exceed 8192 tokens, whatever is asked for
+    assert pkv.plan_partition(4, 8, 16, 100000) <= 8192
+    assert pkv.decode_workspace_bytes(4, 32, 8, 64, 16, 100000, partition_tokens=100000) >= 4 * 32 * 13 * (64 + 2) * 4
     assert pkv.decode_supported("simt", "bf16", 64, 4)
     assert not pkv.decode_supported("simt", "bf16", 96, 4)

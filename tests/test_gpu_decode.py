@@ -43,7 +43,7 @@ def _dev_layer(wl, layer):
 
 
 # partition choices: automatic, one pass, and forced splits of several sizes
-PARTS = {1: [0, 16, 32], 2: [0, 4096, 128, 512], 3: [0, 8192, 256, 1024], 4: [0, 4096, 512], 5: [0, 8192, 256]}
+PARTS = {1: [0, 16, 32], 2: [0, 4096, 128, 512], 3: [0, 8192, 6144, 256, 1024], 4: [0, 4096, 512], 5: [0, 8192, 256]}
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
