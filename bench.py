@@ -3,17 +3,40 @@
 A step is one pass of the whole path over one batch: for every layer of the
 workload, kv_append of this step's token per sequence, then paged decode
 attention over every sequence's context (plus the merge pass when the plan
-splits contexts).  Inputs are seeded synthetic data already resident in HBM.
+splits contexts).  By default each layer is one append_paged_attn_decode
+launch (append fused into the decode kernel); --unfused times the two calls.
+Inputs are seeded synthetic data already resident in HBM.
 
 Default workload: the Llama-3.2-1B-shaped decode batch -- 64 sequences, 32 q /
 8 kv heads, head_dim 64, bf16, block size 16, context lengths uniform in
-[128, 2048].  To keep the 256 MB last-level cache from serving the KV reads,
-the step rotates through R independent copies of the pool, q and outputs
-(R * pool bytes >= 1 GiB).
+[128, 2048].  So that the 256 MB last-level cache cannot serve the KV reads,
+step i uses copy i mod R of the pools, q and outputs, with R copies adding up
+to at least 1 GiB (one-layer workloads; the 16-layer workload is cold by
+itself).
+
+Timing: W warm-up steps, then exactly K steps between two device
+synchronisations, enqueued behind a device-side sleep so that the GPU runs
+them back to back; timing events recorded on the stream the kernels run on
+bracket the K steps.  Fused, a step is one launch per layer, so the per-launch
+duration is the bracketed time over K x layers launches (inter-kernel gaps
+included).  Unfused, events also bracket each decode call (an event between
+two kernels adds idle time, so that figure errs high).
 
 Prints one JSON line on stdout; human-readable details go to stderr.
+
+Other modes (measurement tooling):
+  --copy-calibration  after the timed steps, run a plain device copy of a
+                      known size three times, so that a rocprofv3 --pmc run of
+                      this command also reads the counters of a kernel whose
+                      HBM bytes are known.
+  --pmc-summary FETCH_CSV WRITE_CSV
+                      turn the counter_collection.csv files of two such runs
+                      (FETCH_SIZE, then WRITE_SIZE) into the traffic summary
+                      under profiles/ that later runs report as
+                      roofline.traffic while the decode sources are unchanged.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,10 +50,27 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV GB/s (% of MI355X HBM peak) + decode tokens/s"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s (decimal)
+CSRC = os.path.join(ROOT, "paged_kv_cache_448_amd", "csrc")
+# sources whose change invalidates measured counters of the decode kernels
+DECODE_SOURCES = ["common.h", "kernels.h", "decode_common.h", "decode_mfma_kernel.h", "decode_mfma.hip",
+                  "decode_simt.hip", "merge.hip", "api.cpp"]
+COPY_CALIBRATION_BYTES = 1 << 29  # 512 MiB read and written by the calibration copy
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def decode_sources_sha():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_summary_path(workload_name):
+    return os.path.join(ROOT, "profiles", f"decode_traffic_{workload_name}.txt")
 
 
 def algorithmic_bytes(cfg, lens, tables, block_size):
@@ -86,6 +126,60 @@ def cpu_baseline(wl, budget_s=10.0):
     return dt, runs, blas
 
 
+def _read_counter_csv(path, counter):
+    """(kernel name, value) per dispatch for one counter of a rocprofv3 counter_collection.csv."""
+    import csv
+    rows = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+    return rows
+
+
+def pmc_summary(fetch_csv, write_csv, workload_name, decode_bytes, steps_note):
+    """Traffic per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the calibration copy."""
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter_csv(path, counter)
+        dec = [v for n, v in rows if "decode_mfma_kernel" in n or "decode_simt_kernel" in n]
+        mrg = [v for n, v in rows if "merge_kernel" in n]
+        # the calibration copies are the three largest copy dispatches
+        cpy = sorted(v for n, v in rows if "copy" in n.lower())[-3:]
+        if not dec or not cpy:
+            raise SystemExit(f"{path}: no decode ({len(dec)}) or copy ({len(cpy)}) dispatches with {counter}")
+        copy_kib = float(np.median(cpy))
+        factor = COPY_CALIBRATION_BYTES / (copy_kib * 1024.0)
+        dec_kib = float(np.mean(dec)) + (float(np.mean(mrg)) if mrg else 0.0)
+        out[counter] = {"decode_kib_per_launch": dec_kib, "decode_dispatches": len(dec),
+                        "merge_kib_per_launch": float(np.mean(mrg)) if mrg else 0.0,
+                        "copy_kib_per_dispatch": copy_kib, "copy_bytes": COPY_CALIBRATION_BYTES,
+                        "scale_factor": factor, "bytes_per_launch": dec_kib * 1024.0 * factor}
+    rec = {"workload": workload_name, "decode_sources_sha": decode_sources_sha(),
+           "traffic_bytes_per_launch": out["FETCH_SIZE"]["bytes_per_launch"] + out["WRITE_SIZE"]["bytes_per_launch"],
+           "algorithmic_bytes_per_launch": decode_bytes, "counters": out, "run": steps_note}
+    path = traffic_summary_path(workload_name)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(f"wrote {path}: traffic {rec['traffic_bytes_per_launch'] / 1e6:.1f} MB per launch vs "
+        f"{decode_bytes / 1e6:.1f} MB algorithmic")
+    return rec
+
+
+def load_traffic(workload_name):
+    path = traffic_summary_path(workload_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("decode_sources_sha") != decode_sources_sha():
+        log(f"{path} was measured on other decode sources; traffic not reported")
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,8 +190,11 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = automatic)")
     ap.add_argument("--rotations", type=int, default=0, help="pool copies to rotate through (0 = enough for 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle timing (0 = skip)")
-    ap.add_argument("--eager", action="store_true", help="launch from Python each step instead of HIP graphs")
-    ap.add_argument("--dec-per-graph", type=int, default=8, help="decode calls per captured decode graph")
+    ap.add_argument("--copy-calibration", action="store_true", help="also run a plain copy of known size")
+    ap.add_argument("--unfused", action="store_true", help="time kv_append and paged_attn_decode as two calls")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed steps into one HIP graph and replay it (fused path only)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -105,10 +202,18 @@ def main():
               "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    import workloads
+    if args.pmc_summary:
+        wl = workloads.build(args.config, poison=False)
+        _, unique = algorithmic_bytes(wl.cfg, wl.context_lens, wl.block_tables, wl.cfg.block_size)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name, unique,
+                    f"bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+                    f"--cpu-budget 0 --copy-calibration")
+        return
+
     import torch
 
     import paged_kv_cache_448_amd as pkv
-    import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -151,62 +256,107 @@ def main():
         pkv.paged_attn_decode(t["q"], t["kc"], t["vc"], tables, lens, c.scale, t["out"], max_context_len=mcl,
                               workspace=ws, partition_tokens=args.partition, impl=args.impl)
 
-    def step(i):
-        for t in layers[i % R]:
+    fused = not args.unfused
+    if fused and not pkv.decode_supported("mfma", c.dtype, c.head_dim, c.group):
+        log("the fused append + decode needs the MFMA kernel; timing two calls")
+        fused = False
+    if fused and args.impl == "simt":
+        log("--impl simt: timing two calls (the append is fused into the MFMA kernel only)")
+        fused = False
+
+    def step(i, evs=None):
+        for li, t in enumerate(layers[i % R]):
+            if fused:
+                pkv.append_paged_attn_decode(t["q"], t["kn"], t["vn"], slots, t["kc"], t["vc"], tables, lens, c.scale,
+                                             t["out"], max_context_len=mcl, workspace=ws,
+                                             partition_tokens=args.partition)
+                continue
             pkv.kv_append(t["kn"], t["vn"], slots, t["kc"], t["vc"])
+            if evs is not None:
+                evs[i][li][0].record()
             decode(t)
+            if evs is not None:
+                evs[i][li][1].record()
 
     stream = torch.cuda.current_stream(dev)  # the library launches on the current stream
+    t_host = time.perf_counter()
     for i in range(args.warmup):
         step(i)
+    host_per_step = (time.perf_counter() - t_host) / max(args.warmup, 1)
     torch.cuda.synchronize()
 
-    def timed(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s = torch.cuda.current_stream(dev)
-        e0.record(s)
-        for i in range(n):
-            fn(i)
-        e1.record(s)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
+    # Host-side launches cost about as much time as the GPU work of a step, so
+    # the timed steps are enqueued behind a device-side sleep long enough for
+    # the host to queue all of them: the GPU then runs them back to back and
+    # the events around each decode call bracket only that call's kernels.
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_us = (1 << 20) / max(1e3 * e0.elapsed_time(e1), 1e-3)
+    head_us = max(2000.0, 1.5e6 * host_per_step * K)
+    evs = None if fused else [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                               for _ in range(c.num_layers)] for _ in range(K)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
-    eager_ms = timed(step, args.steps)
-
-    # The same work replayed from HIP graphs (one per rotation), which removes
-    # the Python binding's per-call host time from the GPU's critical path.
-    # Inside capture the library launches on the capture stream.
-    gstep, gdec = [], []
-    if not args.eager:
-        for r in range(R):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(r)
-            gstep.append(g)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for _ in range(args.dec_per_graph):
-                    decode(layers[r][0])
-            gdec.append(g)
-        for r in range(R):
-            gstep[r].replay()
-            gdec[r].replay()
+    graph = None
+    if args.graph and fused:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(K):
+                step(i)
+        graph.replay()  # untimed: uploads the graph
         torch.cuda.synchronize()
-        ms_step = timed(lambda i: gstep[i % R].replay(), args.steps)
-        dec_us = 1e3 * timed(lambda i: gdec[i % R].replay(), args.steps) / args.dec_per_graph
+
+    # timed region: exactly K steps between two synchronisations
+    torch.cuda.synchronize()
+    if graph is None:
+        torch.cuda._sleep(int(head_us * cycles_per_us))
+    t_begin.record(stream)
+    t_host = time.perf_counter()
+    if graph is not None:
+        graph.replay()
     else:
-        ms_step = eager_ms
-        dec_us = 1e3 * timed(lambda i: decode(layers[i % R][0]), args.steps)
-    log(f"eager step {eager_ms * 1e3:.1f} us, {'graph' if not args.eager else 'eager'} step {ms_step * 1e3:.1f} us")
+        for i in range(K):
+            step(i, evs)
+    host_us = 1e6 * (time.perf_counter() - t_host)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / K
+    launch = "one HIP graph of the K steps" if graph is not None else "eager, queued ahead of the GPU"
+    if graph is None and host_us > head_us + 1e3 * ms_step * K:
+        launch = "eager, host-bound (GPU may have idled between steps)"
+        log(f"warning: enqueueing took {host_us:.0f} us, more than the {head_us:.0f} us head start plus GPU time")
+    if fused:
+        dec_us = 1e3 * ms_step / c.num_layers
+        log(f"step {ms_step * 1e3:.1f} us ({c.num_layers} layer(s), one fused launch each): {dec_us:.2f} us per "
+            f"launch; host enqueue {host_us:.0f} us behind a {head_us:.0f} us head start")
+    else:
+        dec_us_all = [1e3 * a.elapsed_time(b) for per_step in evs for (a, b) in per_step]
+        dec_us = float(np.mean(dec_us_all))
+        log(f"step {ms_step * 1e3:.1f} us ({c.num_layers} layer(s)); decode call mean {dec_us:.2f} us, "
+            f"median {float(np.median(dec_us_all)):.2f}, min {min(dec_us_all):.2f}, max {max(dec_us_all):.2f} "
+            f"over {len(dec_us_all)} calls; host enqueue {host_us:.0f} us behind a {head_us:.0f} us head start")
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     logical, unique = algorithmic_bytes(c, wl.context_lens, wl.block_tables, c.block_size)
     app = append_bytes(c, B)
     step_bytes = c.num_layers * (unique + app)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    dec_gbs = unique / (dec_us * 1e-6) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us ({c.num_layers} layers), decode call {dec_us:.1f} us "
-        f"; decode bytes {unique / 1e6:.2f} MB unique, "
-        f"{logical / 1e6:.2f} MB logical -> {dec_gbs:.0f} GB/s = {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak")
+    launch_bytes = unique + app if fused else unique  # the fused launch also moves the appended tokens
+    dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
+    log(f"decode bytes {unique / 1e6:.2f} MB unique, {logical / 1e6:.2f} MB logical per layer; "
+        f"{launch_bytes / 1e6:.2f} MB per launch -> {dec_gbs:.0f} GB/s = {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak; "
+        f"step {value:.0f} GB/s")
 
     cpu = None
     if args.cpu_budget > 0:
@@ -218,12 +368,19 @@ def main():
                "tokens_per_s": round(B / dt, 2)}
         log(f"cpu oracle: {dt:.3f} s per pass over {B} sequences ({runs} passes)")
 
+    traffic = load_traffic(c.name) if fused else None
+    if fused:
+        kernel_desc = ("decode_mfma_kernel with the append fused, one launch per layer" if part == 0 else
+                       "append_paged_attn_decode call: partition kernel (append fused) + merge kernel")
+    else:
+        kernel_desc = ("paged_attn_decode call, one kernel" if part == 0 else
+                       "paged_attn_decode call: partition kernel + merge kernel")
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
@@ -243,12 +400,14 @@ def main():
         "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1),
         "decode_call_us": round(dec_us, 2),
         "decode_bytes_unique": unique,
+        "launch_bytes": launch_bytes,
         "decode_bytes_logical": logical,
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged_attn_decode call (partition kernel + merge pass when split)"},
-        "launch": "eager" if args.eager else "hip-graph",
-        "eager_ms_per_step": round(eager_ms, 5),
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(round(traffic)),
+                     "kernel": kernel_desc},
+        "launch": launch,
+        "append": "fused into the decode kernel" if fused else "separate kv_append kernel",
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

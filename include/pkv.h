@@ -146,6 +146,8 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  *                     each processed by its own workgroup, and the partial
  *                     results are combined by a log-sum-exp merge pass.  A value
  *                     >= max_context_len means a single pass without merge.
+ *                     Partitions are at most 8192 tokens: larger values (and a
+ *                     single pass over longer contexts) are cut to 8192.
  *   impl              PKV_IMPL_AUTO, PKV_IMPL_SIMT (vector-ALU dot products) or
  *                     PKV_IMPL_MFMA (matrix-core tiles).
  * Results of all choices agree to fp32 rounding.
@@ -157,6 +159,39 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
                              void* workspace, size_t workspace_bytes, int32_t partition_tokens,
                              int32_t impl, hipStream_t stream);
+
+/*
+ * pkv_append_paged_attn_decode -- one decode step of one layer in a single
+ * launch: pkv_kv_append of one new token per sequence, then
+ * pkv_paged_attn_decode over contexts that include it.
+ *
+ *   k_new, v_new  [num_seqs][num_kv_heads][head_dim]: K and V of the token
+ *                 being decoded by each sequence.
+ *   slot_mapping  [num_seqs] int64: slot_mapping[i] is the slot of position
+ *                 context_lens[i] - 1 of sequence i (its last block-table
+ *                 block, offset (L_i - 1) % block_size), where the token is
+ *                 written; a negative slot means "append nothing for this
+ *                 sequence".  That slot must lie in no other sequence's
+ *                 context (a block manager guarantees it for the block a
+ *                 sequence is still filling).
+ *   the other arguments are those of pkv_paged_attn_decode_ex (MFMA kernel).
+ *
+ * Results, when the preconditions hold: the pools and out are bit-identical
+ * to pkv_kv_append(k_new, v_new, slot_mapping, B, ...) followed by
+ * pkv_paged_attn_decode_ex(..., impl = PKV_IMPL_MFMA).  A non-negative slot
+ * that is not the slot of position L_i - 1 (or a sequence with L_i = 0 and a
+ * slot) writes nothing and makes sequence i's output NaN; the kernel cannot
+ * report it otherwise.
+ * Supported: as the MFMA kernel (pkv_decode_supported(PKV_IMPL_MFMA, ...)).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE, PKV_E_UNSUPPORTED, PKV_E_WORKSPACE, PKV_E_HIP.
+ */
+int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream);
 
 /*
  * pkv_decode_plan_partition -- the partition size (tokens) the automatic choice

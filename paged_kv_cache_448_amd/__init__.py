@@ -9,6 +9,8 @@ Names mirror the C ABI in include/pkv.h and include/pkv_alloc.h:
 
 * ``kv_append(k, v, slot_mapping, k_cache, v_cache)``
 * ``paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
+* ``append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+  context_lens, scale, out)`` -- both in one launch (one decode step of one layer)
 * ``BlockAllocator`` -- the host-side block allocator.
 
 Caches are tensors of shape ``(num_blocks, num_kv_heads, block_size // 16, 16 * head_dim)``
@@ -22,7 +24,7 @@ import torch
 
 from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
 
-__all__ = ["kv_append", "paged_attn_decode", "decode_workspace_bytes", "decode_supported", "plan_partition", "new_cache",
+__all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes", "decode_supported", "plan_partition", "new_cache",
            "cache_dims", "BlockAllocator", "PkvError", "lib"]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
@@ -142,6 +144,51 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
         ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N, _dtype_code(q), _ptr(workspace),
         ctypes.c_size_t(workspace.numel()), int(partition_tokens), IMPLS[impl], _stream(q)))
+    return out
+
+
+def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
+                             out=None, *, max_context_len=None, workspace=None, partition_tokens=0):
+    """kv_append of one token per sequence, then paged_attn_decode, in one launch.
+
+    k_new, v_new: [B, Hkv, D]; slot_mapping: int64 [B], the slot of position
+    context_lens[i] - 1 of sequence i (negative: nothing appended for it).
+    Same result as the two calls when that holds; a slot that is not that
+    position's slot is not written and makes sequence i's output NaN.
+    """
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(q, "q", k_cache.dtype, 3)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _device_tensor(t, name, k_cache.dtype, 3)
+        _need(tuple(t.shape) == (B, Hkv, D), f"{name} must be [{B}, {Hkv}, {D}], got {tuple(t.shape)}")
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+    _need(slot_mapping.shape[0] == B, "slot_mapping must have one slot per sequence")
+    _device_tensor(k_cache, "k_cache")
+    _device_tensor(v_cache, "v_cache")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    check(lib().pkv_append_paged_attn_decode(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
+        _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
+        _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
     return out
 
 

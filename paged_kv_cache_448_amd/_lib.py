@@ -22,6 +22,9 @@ PROTOTYPES = {
                                          _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _vp]),
     "pkv_paged_attn_decode_ex": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _i32, _i32, _vp]),
+    "pkv_append_paged_attn_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp,
+                                                _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _i32,
+                                                _vp]),
     "pkv_decode_plan_partition": (_i32, [_i32] * 4),
     "pkv_decode_supported": (_c.c_int, [_i32] * 4),
     "pkv_alloc_create": (_vp, [_i32, _i32, _c.c_uint64]),

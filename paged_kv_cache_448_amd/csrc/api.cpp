@@ -136,13 +136,21 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                        max_context_len, 0);
 }
 
-int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* block_tables, int32_t max_blocks_per_seq,
-                             const int32_t* context_lens, int32_t max_context_len, float scale,
-                             void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
-                             void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                             int32_t impl, hipStream_t stream) {
+namespace {
+
+// Shared body of the decode entry points; `app` carries the fused append
+// (k_new, v_new, slot_mapping) or nulls.
+struct FusedAppend {
+  const void* k_new;
+  const void* v_new;
+  const int64_t* slot_mapping;
+};
+
+int decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
+                void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace, size_t workspace_bytes,
+                int32_t partition_tokens, int32_t impl, const FusedAppend& app, hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_E_SHAPE;
@@ -151,9 +159,12 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
     return PKV_E_SHAPE;
   if (partition_tokens < 0 || partition_tokens % 16) return PKV_E_SHAPE;
   if (!dtype_ok(dtype) || !block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  // sub-tile indices of the pool are 32-bit inside the kernels
+  if (static_cast<int64_t>(num_blocks) * num_kv_heads * (block_size / 16) > INT_MAX) return PKV_E_SHAPE;
   const int32_t group = num_q_heads / num_kv_heads;
   const bool simt_ok = pkv::simt_supported(dtype, head_dim, group);
   const bool mfma_ok = pkv::mfma_supported(dtype, head_dim, group);
+  const bool fused = app.slot_mapping != nullptr;
   bool use_mfma;
   switch (impl) {
     case PKV_IMPL_AUTO:
@@ -170,9 +181,12 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
       break;
     default: return PKV_E_UNSUPPORTED;
   }
+  if (fused && !use_mfma) return PKV_E_UNSUPPORTED;  // the append is fused into the MFMA kernel only
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
+  if (fused && (!app.k_new || !app.v_new)) return PKV_E_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_E_SHAPE;
+  if (fused && (!aligned16(app.k_new) || !aligned16(app.v_new))) return PKV_E_SHAPE;
 
   const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
   const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, plan);
@@ -198,6 +212,11 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
     p.part_m = reinterpret_cast<float*>(ws + align256(rows * head_dim * sizeof(float)));
     p.part_l = reinterpret_cast<float*>(ws + align256(rows * head_dim * sizeof(float)) + align256(rows * sizeof(float)));
   }
+  p.k_new = static_cast<const uint16_t*>(app.k_new);
+  p.v_new = static_cast<const uint16_t*>(app.v_new);
+  p.slot_mapping = app.slot_mapping;
+  p.k_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
+  p.v_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -217,6 +236,34 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
     if (e != hipSuccess) return PKV_E_HIP;
   }
   return PKV_OK;
+}
+
+}  // namespace
+
+int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len, float scale,
+                             void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                             void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                             int32_t impl, hipStream_t stream) {
+  return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
+                     workspace_bytes, partition_tokens, impl, FusedAppend{nullptr, nullptr, nullptr}, stream);
+}
+
+int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v_new,
+                                 const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace,
+                                 size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream) {
+  if (num_seqs > 0 && !slot_mapping) return PKV_E_NULL;
+  return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
+                     workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping},
+                     stream);
 }
 
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,

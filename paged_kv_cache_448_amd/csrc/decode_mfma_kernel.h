@@ -38,6 +38,9 @@
 //
 // Partitions of one (sequence, kv head) store their softmax states and the
 // merge kernel (merge.hip) folds them.
+//
+// Optionally the kernel also performs the step's KV append (see the fused
+// append block below), so a decode step is one launch per layer.
 #pragma once
 
 #include "decode_common.h"
@@ -94,6 +97,7 @@ template <int D> struct Tile {
 template <typename T, int D, int G, int NW, int S>
 __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
+  static_assert(NW * kWave >= D, "one thread per dimension stages the appended token");
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
@@ -102,7 +106,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
   if (bad_len || L == 0) {
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len);
+    // an appended token needs a position: L = 0 with a slot is a caller error
+    const bool orphan = p.slot_mapping != nullptr && p.slot_mapping[w.seq] >= 0;
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan);
     return;
   }
   const int start = w.part * p.part_tokens;
@@ -125,6 +131,17 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
     }
   }
 
+  // K and V of the token appended this step (fused append, below); read
+  // before the block-table window so that both are in flight together.
+  u32x4 krun = {0u, 0u, 0u, 0u};
+  uint16_t vnew = 0;
+  if (p.slot_mapping != nullptr) {
+    const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
+    const int ti = static_cast<int>(threadIdx.x);
+    krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(ti, D / 8 - 1));
+    vnew = p.v_new[row * D + min(ti, D - 1)];
+  }
+
   // lane k: index of this wave's k-th sub-tile in the pool (sub-tiles of 16*D
   // elements, numbered (block*Hkv + kvh)*(bs/16) + sub-tile in block), or -1
   // when the table names a block outside the pool.
@@ -138,6 +155,42 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
               : -1;
   }
   bool bad = false;
+
+  // Fused append of the token decoded this step, which sits at position L-1.
+  // Its K and V were read together with the block-table window, so the
+  // append adds no dependent round trip before the first sub-tile loads.  The
+  // workgroup whose partition holds L-1 stages the token in LDS, and the wave
+  // that reads that sub-tile puts it into its registers in place of whatever
+  // the load returned; the same workgroup stores the token into the pools (the
+  // same bytes kv_append writes) after its sub-tile loop, where nothing waits
+  // for the stores.  A slot that is not the slot of L-1 is not written and makes the
+  // sequence's output NaN (every workgroup of the sequence checks).
+  __shared__ __align__(16) uint16_t sm_new[2][D];  // the appended token's K and V
+  int app_w = -1, app_k = -1, app_r = 0;           // wave, step and token row that hold it
+  int64_t app_sub = -1;                            // pool sub-tile of the slot, when this workgroup writes it
+  if (p.slot_mapping != nullptr) {
+    const int app_pos = L - 1;
+    const int ti = static_cast<int>(threadIdx.x);
+    const int64_t slot = p.slot_mapping[w.seq];
+    const int blk = app_pos / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
+    const int off = app_pos - blk * p.block_size;
+    if (slot >= 0) {
+      if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
+          slot != static_cast<int64_t>(phys) * p.block_size + off) {
+        bad = true;
+      } else if (app_pos >= start && app_pos < end) {
+        app_sub = (static_cast<int64_t>(phys) * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + (off >> 4);
+        app_r = off & 15;
+        if (ti < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * ti]) = krun;
+        if (ti < D) sm_new[1][ti] = vnew;
+        const int s_tok = (app_pos - start) >> 4;
+        app_w = s_tok % NW;
+        app_k = s_tok / NW;
+      }
+    }
+    __syncthreads();
+  }
 
   // Branch-free, so that every path issues the same loads and the compiler's
   // wait counts keep S-1 sub-tiles in flight.  A bad block id makes the
@@ -163,6 +216,23 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
   // k-th sub-tile of this wave; k >= n_w is an empty pad step (every token
   // masked), which leaves the state unchanged since k = 0 is never empty.
   auto compute = [&](int k, Tile<D>& t) {
+    if (k == app_k && wv == app_w) {
+      // token row app_r of this sub-tile is the appended token
+      if (r == app_r) {
+#pragma unroll
+        for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(&sm_new[0][(4 * j + kg) * 8]);
+      }
+      if (kg == (app_r >> 2)) {
+        const int sh = (app_r & 1) * 16;
+        const uint32_t keep = ~(0xffffu << sh);
+#pragma unroll
+        for (int j = 0; j < JV; ++j) {
+          const uint32_t v = static_cast<uint32_t>(sm_new[1][16 * j + r]) << sh;
+          if (app_r & 2) t.v[j].y = (t.v[j].y & keep) | v;
+          else t.v[j].x = (t.v[j].x & keep) | v;
+        }
+      }
+    }
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[j], sc);
@@ -197,11 +267,11 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
     for (int j = 0; j < JV; ++j) o[j] = Mma<T>::pv(t.v[j], pop, o[j]);
   };
 
+  // S register slots; slot i holds sub-tiles i, i+S, i+2S, ...  Steps past
+  // n_w re-load the wave's last sub-tile (a cache hit) and compute it as an
+  // empty pad step, so the loop body is the same straight-line code every
+  // time and the compiler's wait counts stay S-1 sub-tiles deep.
   if (n_w > 0) {
-    // S register slots; slot i holds sub-tiles i, i+S, i+2S, ...  Steps past
-    // n_w re-load the wave's last sub-tile (a cache hit) and compute it as an
-    // empty pad step, so the loop body is the same straight-line code every
-    // time and the compiler's wait counts stay S-1 sub-tiles deep.
     Tile<D> t[S];
     const int last = n_w - 1;
 #pragma unroll
@@ -217,6 +287,14 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
     }
 #pragma unroll
     for (int i = 0; i < S; ++i) compute(kb + i, t[i]);
+  }
+
+  if (app_sub >= 0) {
+    const int ti = static_cast<int>(threadIdx.x);
+    const size_t sub = static_cast<size_t>(app_sub);
+    if (ti < D / 8)
+      *reinterpret_cast<u32x4*>(p.k_cache_w + ((sub * (D / 8) + ti) * 16 + app_r) * 8) = krun;
+    if (ti < D) p.v_cache_w[(sub * D + ti) * 16 + app_r] = vnew;
   }
 
   // fold the four token rows (kg) of the denominator

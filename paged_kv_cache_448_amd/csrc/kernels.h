@@ -26,6 +26,14 @@ struct DecodeParams {
   float* part_o;                 // [B, Hq, num_parts, D]  (only when num_parts > 1)
   float* part_m;                 // [B, Hq, num_parts]     running max, log2 units
   float* part_l;                 // [B, Hq, num_parts]     softmax denominator
+  // Fused append (MFMA kernel only): token i of this step, k_new[i] / v_new[i]
+  // ([B, Hkv, D]), goes into slot slot_mapping[i], which must be the slot of
+  // position L_i - 1 of sequence i; slot_mapping == nullptr: no append.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int64_t* slot_mapping;
+  uint16_t* k_cache_w;           // the same pools, writable
+  uint16_t* v_cache_w;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int32_t max_blocks_per_seq, max_context_len;
   int32_t part_tokens;           // tokens per partition, a multiple of 16

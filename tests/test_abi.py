@@ -101,3 +101,23 @@ def test_workspace_and_plan():
     assert pkv.decode_workspace_bytes(4, 32, 8, 64, 16, 100000, partition_tokens=100000) >= 4 * 32 * 13 * (64 + 2) * 4
     assert pkv.decode_supported("simt", "bf16", 64, 4)
     assert not pkv.decode_supported("simt", "bf16", 96, 4)
+
+
+def _fused(**kw):
+    a = dict(q=16, kn=16, vn=16, sm=16, kc=16, vc=16, bt=16, mb=4, cl=16, mcl=64, scale=0.125, out=16, B=2, Hq=4,
+             Hkv=2, D=64, bs=16, N=8, dt=0, ws=NULL, wsb=0, pt=0)
+    a.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return pkv.lib().pkv_append_paged_attn_decode(
+        p(a["q"]), p(a["kn"]), p(a["vn"]), p(a["sm"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]),
+        a["mcl"], ctypes.c_float(a["scale"]), p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["N"],
+        a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sm=NULL), E_NULL), (dict(kn=NULL), E_NULL), (dict(vn=NULL), E_NULL), (dict(q=NULL), E_NULL),
+    (dict(kn=24), E_SHAPE), (dict(Hq=6, Hkv=4), E_SHAPE), (dict(D=96), E_UNSUPPORTED), (dict(dt=3), E_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2), E_UNSUPPORTED), (dict(B=0, sm=NULL), OK),
+])
+def test_fused_append_decode_rejects_bad_arguments_before_launch(kw, status):
+    assert _fused(**kw) == status
