@@ -127,13 +127,13 @@ def cpu_baseline(wl, budget_s=10.0):
 
 
 def _read_counter_csv(path, counter):
-    """(kernel name, value) per dispatch for one counter of a rocprofv3 counter_collection.csv."""
+    """(kernel name, grid size, value) per dispatch for one counter of a rocprofv3 counter_collection.csv."""
     import csv
     rows = []
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             if r.get("Counter_Name") == counter:
-                rows.append((r.get("Kernel_Name", ""), float(r["Counter_Value"])))
+                rows.append((r.get("Kernel_Name", ""), int(r.get("Grid_Size", 0)), float(r["Counter_Value"])))
     return rows
 
 
@@ -143,10 +143,14 @@ def pmc_summary(fetch_csv, write_csv, workload_name, decode_bytes, steps_note):
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _read_counter_csv(path, counter)
-        dec = [v for n, v in rows if "decode_mfma_kernel" in n or "decode_simt_kernel" in n]
-        mrg = [v for n, v in rows if "merge_kernel" in n]
+        # the timed launches: with the fused append the grid carries extra append
+        # workgroups, which tells them from the decode-only context loop
+        dec_rows = [(g, v) for n, g, v in rows if "decode_mfma_kernel" in n or "decode_simt_kernel" in n]
+        top = max((g for g, _ in dec_rows), default=0)
+        dec = [v for g, v in dec_rows if g == top]
+        mrg = [v for n, g, v in rows if "merge_kernel" in n]
         # the calibration copies are the three largest copy dispatches
-        cpy = sorted(v for n, v in rows if "copy" in n.lower())[-3:]
+        cpy = sorted(v for n, g, v in rows if "copy" in n.lower())[-3:]
         if not dec or not cpy:
             raise SystemExit(f"{path}: no decode ({len(dec)}) or copy ({len(cpy)}) dispatches with {counter}")
         copy_kib = float(np.median(cpy))
@@ -340,6 +344,22 @@ def main():
             f"median {float(np.median(dec_us_all)):.2f}, min {min(dec_us_all):.2f}, max {max(dec_us_all):.2f} "
             f"over {len(dec_us_all)} calls; host enqueue {host_us:.0f} us behind a {head_us:.0f} us head start")
 
+    # Context, outside the K timed steps: the decode kernel alone (no append),
+    # K calls back to back over the rotating copies, events around all of them.
+    decode_only_us = None
+    if True:
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(head_us * cycles_per_us))
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(K):
+            for t in layers[i % R]:
+                decode(t)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        decode_only_us = 1e3 * d0.elapsed_time(d1) / (K * c.num_layers)
+        log(f"decode kernel alone (separate loop, context): {decode_only_us:.2f} us per call")
+
     if args.copy_calibration:
         src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -406,6 +426,8 @@ def main():
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(round(traffic)),
                      "kernel": kernel_desc},
+        "decode_only_call_us": None if decode_only_us is None else round(decode_only_us, 2),
+        "decode_only_hbm_frac": None if decode_only_us is None else round(unique / (decode_only_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "launch": launch,
         "append": "fused into the decode kernel" if fused else "separate kv_append kernel",
         "cpu_baseline": cpu,

@@ -217,6 +217,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.slot_mapping = app.slot_mapping;
   p.k_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   p.v_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
+  p.append_wgs = 0;  // set by the MFMA launcher for fused calls
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;

@@ -19,9 +19,10 @@ struct WorkItem {
 };
 
 // Items are ordered (sequence, partition, kv head); see xcd_remap for the
-// workgroup -> item order.
-__device__ __forceinline__ WorkItem decode_item(const DecodeParams& p) {
-  int it = xcd_remap(blockIdx.x, gridDim.x);
+// workgroup -> item order.  bid / n: this workgroup's index among the n
+// decode workgroups of the launch.
+__device__ __forceinline__ WorkItem decode_item(const DecodeParams& p, int bid, int n) {
+  int it = xcd_remap(bid, n);
   WorkItem w;
   w.kvh = it % p.num_kv_heads;
   it /= p.num_kv_heads;

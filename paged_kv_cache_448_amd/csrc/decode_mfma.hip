@@ -5,22 +5,44 @@ namespace pkv {
 
 namespace {
 
-// Sub-tiles each wave keeps in flight.
-constexpr int kMfmaDepth = 4;
+// Sub-tiles each wave keeps in flight, and the waves per SIMD the register
+// allocation must leave room for (measured on the Llama-3.2-1B batch and the
+// LLaMA-2-70B layer): four sub-tiles (16 KB) at head_dim 64 with the
+// compiler's own allocation (three waves per SIMD; forcing four costs more in
+// scheduling than it gains), two sub-tiles (16 KB) at head_dim 128 at three
+// waves per SIMD, the most that does not spill.
+template <int D> struct MfmaShape;
+template <> struct MfmaShape<64> { static constexpr int kDepth = 4, kMinWaves = 2; };
+template <> struct MfmaShape<128> { static constexpr int kDepth = 2, kMinWaves = 3; };
 
 // Whole contexts and partitions above kFourWaveMaxTokens run with 8 waves per
 // workgroup, shorter partitions with 4 (each wave may own at most 64
 // sub-tiles of a partition).
 template <typename T, int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
-  const int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
+  constexpr int S = MfmaShape<D>::kDepth, W = MfmaShape<D>::kMinWaves;
+  int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
   if (p.part_tokens > kMaxPartitionTokens) return hipErrorInvalidValue;
-  if (p.num_parts == 1 || p.part_tokens > kFourWaveMaxTokens) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, kMfmaDepth>), dim3(static_cast<unsigned>(items)),
-                       dim3(8 * kWave), 0, stream, p);
+  const int nw = (p.num_parts == 1 || p.part_tokens > kFourWaveMaxTokens) ? 8 : 4;
+  DecodeParams q = p;
+  q.append_wgs = 0;
+  if (p.slot_mapping != nullptr) {
+    // leading append workgroups: one thread per (token, kv head, 8-dim run),
+    // at most 256 workgroups, a multiple of 8 so the decode workgroups keep
+    // their XCD placement
+    const int64_t threads = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * (D / 8);
+    int64_t wgs = (threads + nw * kWave - 1) / (nw * kWave);
+    wgs = ((wgs < 256 ? wgs : 256) + 7) / 8 * 8;
+    q.append_wgs = static_cast<int32_t>(wgs);
+    items += wgs;
+  }
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  if (nw == 8) {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W>), dim3(static_cast<unsigned>(items)), dim3(8 * kWave),
+                       0, stream, q);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, kMfmaDepth>), dim3(static_cast<unsigned>(items)),
-                       dim3(4 * kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W>), dim3(static_cast<unsigned>(items)), dim3(4 * kWave),
+                       0, stream, q);
   }
   return hipGetLastError();
 }

@@ -87,6 +87,10 @@ template <> struct Mma<Fp16> {
   }
 };
 
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data, no
+// swizzle); with stride 0 and range 0xffffffff the buffer is a plain byte range.
+constexpr int kBufferConfig = 0x00020000;
+
 // The registers one sub-tile needs: K operands (one per 32 dims) and V
 // operands (one per 16 dims).
 template <int D> struct Tile {
@@ -94,15 +98,59 @@ template <int D> struct Tile {
   u32x2 v[D / 16];
 };
 
-template <typename T, int D, int G, int NW, int S>
-__global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p) {
+// Fused append, store side: the same bytes kv_append writes for token i =
+// sequence i, after the checks the decode side makes (a valid length, and the
+// slot is the slot of position L_i - 1); thread per (token, kv head, 8-dim run)
+// as in kv_append, grid-strided over the append workgroups.
+template <int D, int NT>
+__device__ __forceinline__ void append_tokens(const DecodeParams& p) {
+  constexpr int runs = D / 8;
+  const int64_t total = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * runs;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < total;
+       i += static_cast<int64_t>(p.append_wgs) * NT) {
+    const int c = static_cast<int>(i % runs);
+    const int64_t th = i / runs;  // sequence * Hkv + kv head
+    const int h = static_cast<int>(th % p.num_kv_heads);
+    const int t = static_cast<int>(th / p.num_kv_heads);
+    const int64_t slot = p.slot_mapping[t];
+    const int L = p.context_lens[t];
+    if (slot < 0 || L <= 0 || bad_length(L, p)) continue;
+    const int pos = L - 1;
+    const int blk = pos / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(t) * p.max_blocks_per_seq + blk];
+    const int off = pos - blk * p.block_size;
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
+        slot != static_cast<int64_t>(phys) * p.block_size + off)
+      continue;
+    const size_t sub = (static_cast<size_t>(phys) * p.num_kv_heads + h) * (p.block_size >> 4) + (off >> 4);
+    const int r = off & 15;
+    const u32x4 kk = *reinterpret_cast<const u32x4*>(p.k_new + th * D + c * 8);
+    const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v_new + th * D + c * 8);
+    *reinterpret_cast<u32x4*>(p.k_cache_w + ((sub * runs + c) * 16 + r) * 8) = kk;
+    uint16_t* vb = p.v_cache_w + (sub * D + c * 8) * 16 + r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vb[(2 * e) * 16] = static_cast<uint16_t>(vv[e] & 0xffffu);
+      vb[(2 * e + 1) * 16] = static_cast<uint16_t>(vv[e] >> 16);
+    }
+  }
+}
+
+// MINW: waves per SIMD the register allocation must allow (launch-bound
+// minimum); the launcher picks S and MINW per head size so that nothing spills.
+template <typename T, int D, int G, int NW, int S, int MINW>
+__global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
   static_assert(NW * kWave >= D, "one thread per dimension stages the appended token");
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int r = lane & 15, kg = lane >> 4;
-  const WorkItem w = decode_item(p);
+  if (static_cast<int>(blockIdx.x) < p.append_wgs) {
+    append_tokens<D, NW * kWave>(p);
+    return;
+  }
+  const WorkItem w = decode_item(p, blockIdx.x - p.append_wgs, gridDim.x - p.append_wgs);
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
   if (bad_len || L == 0) {
@@ -133,13 +181,19 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
 
   // K and V of the token appended this step (fused append, below); read
   // before the block-table window so that both are in flight together.
+  // The slot and the physical block of position L-1 are read here too, so the
+  // check below costs no round trip of its own.
   u32x4 krun = {0u, 0u, 0u, 0u};
   uint16_t vnew = 0;
+  int64_t app_slot = -1;
+  int app_phys = 0;
   if (p.slot_mapping != nullptr) {
     const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
     const int ti = static_cast<int>(threadIdx.x);
     krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(ti, D / 8 - 1));
     vnew = p.v_new[row * D + min(ti, D - 1)];
+    app_slot = p.slot_mapping[w.seq];
+    app_phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + (L - 1) / p.block_size];
   }
 
   // lane k: index of this wave's k-th sub-tile in the pool (sub-tiles of 16*D
@@ -167,20 +221,18 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
   // sequence's output NaN (every workgroup of the sequence checks).
   __shared__ __align__(16) uint16_t sm_new[2][D];  // the appended token's K and V
   int app_w = -1, app_k = -1, app_r = 0;           // wave, step and token row that hold it
-  int64_t app_sub = -1;                            // pool sub-tile of the slot, when this workgroup writes it
   if (p.slot_mapping != nullptr) {
     const int app_pos = L - 1;
     const int ti = static_cast<int>(threadIdx.x);
-    const int64_t slot = p.slot_mapping[w.seq];
+    const int64_t slot = app_slot;
     const int blk = app_pos / p.block_size;
-    const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
+    const int phys = app_phys;
     const int off = app_pos - blk * p.block_size;
     if (slot >= 0) {
       if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
           slot != static_cast<int64_t>(phys) * p.block_size + off) {
         bad = true;
       } else if (app_pos >= start && app_pos < end) {
-        app_sub = (static_cast<int64_t>(phys) * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + (off >> 4);
         app_r = off & 15;
         if (ti < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * ti]) = krun;
         if (ti < D) sm_new[1][ti] = vnew;
@@ -196,16 +248,26 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
   // wait counts keep S-1 sub-tiles in flight.  A bad block id makes the
   // whole head group NaN, so what is read in its place (sub-tile 0 of the
   // pool, always in bounds) does not matter.
+  //
+  // Buffer loads: the sub-tile's base address lives in a wave-uniform
+  // resource (scalar registers) and each lane keeps two constant byte
+  // offsets, so no per-load address occupies vector registers.
+  const int koff = ((kg * 16) + r) * 16;     // K run kg of token r; + 1 KB (scalar offset) per j
+  const int voff = r * 32 + kg * 8;          // V dim r, tokens 4kg..4kg+3; + 512 B per j
   auto load = [&](int k, Tile<D>& t) {
     int sub = __builtin_amdgcn_readlane(tid, k);
     bad |= sub < 0;
     sub = max(sub, 0);
     const uint16_t* kt = p.k_cache + static_cast<size_t>(sub) * (16 * D);
     const uint16_t* vt = p.v_cache + static_cast<size_t>(sub) * (16 * D);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kt), 0, -1, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vt), 0, -1, kBufferConfig);
 #pragma unroll
-    for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(kt + ((4 * j + kg) * 16 + r) * 8);
+    for (int j = 0; j < JK; ++j)
+      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 1024 * j, 0));
 #pragma unroll
-    for (int j = 0; j < JV; ++j) t.v[j] = *reinterpret_cast<const u32x2*>(vt + (16 * j + r) * 16 + 4 * kg);
+    for (int j = 0; j < JV; ++j)
+      t.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 512 * j, 0));
   };
 
   float m = -INFINITY, l = 0.f;
@@ -241,8 +303,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 4 * kg + i < nvalid ? sc[i] * p.scale_log2 : -INFINITY;
     float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = fmaxf(bm, shfl_xor(bm, 16));
-    bm = fmaxf(bm, shfl_xor(bm, 32));
+    bm = max_xor32(max_xor16(bm));
     const float mn = fmaxf(m, bm);
     const float al = fast_exp2(m - mn);
     m = mn;
@@ -289,17 +350,8 @@ __global__ __launch_bounds__(NW * kWave) void decode_mfma_kernel(DecodeParams p)
     for (int i = 0; i < S; ++i) compute(kb + i, t[i]);
   }
 
-  if (app_sub >= 0) {
-    const int ti = static_cast<int>(threadIdx.x);
-    const size_t sub = static_cast<size_t>(app_sub);
-    if (ti < D / 8)
-      *reinterpret_cast<u32x4*>(p.k_cache_w + ((sub * (D / 8) + ti) * 16 + app_r) * 8) = krun;
-    if (ti < D) p.v_cache_w[(sub * D + ti) * 16 + app_r] = vnew;
-  }
-
   // fold the four token rows (kg) of the denominator
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
+  l = add_xor32(add_xor16(l));
   if (bad) l = __int_as_float(0x7fc00000);
   if (r < G) {
     if (kg == 0) {
