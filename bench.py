@@ -233,7 +233,7 @@ def main():
         t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt)
         return (t.reshape(shape) if shape else t).to(dev)
 
-    shape = (wl.num_blocks, c.num_kv_heads, c.block_size // 16, 16 * c.head_dim)
+    shape = (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
     pool_bytes = 2 * int(np.prod(shape)) * c.elem_bytes * c.num_layers
     R = args.rotations or (1 if c.num_layers > 1 else max(1, math.ceil((1 << 30) / pool_bytes)))
     layers = []  # [rotation][layer] -> dict of device tensors

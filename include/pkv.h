@@ -37,15 +37,11 @@
  * Cache layout (both caches hold N blocks of bs tokens, bs a multiple of 16;
  * the block is the outermost index, so block n is one contiguous range):
  *
- *   k_cache: [N][Hkv][bs/16][D/8][16][8]   K[n,h,t,d] at
- *            ((((n*Hkv + h)*(bs/16) + t/16)*(D/8) + d/8)*16 + t%16)*8 + d%8
- *   v_cache: [N][Hkv][bs/16][D][16]        V[n,h,t,d] at
- *            (((n*Hkv + h)*(bs/16) + t/16)*D + d)*16 + t%16
+ *   k_cache, v_cache: [N][Hkv][bs][D]   K[n,h,t,d] and V[n,h,t,d] at
+ *            ((n*Hkv + h)*bs + t)*D + d
  *
- * i.e. every (block, kv head) is split into 16-token sub-tiles of 16*D
- * elements; inside a K sub-tile, 8 consecutive dims of one token form a
- * 16-byte run and the runs of the 16 tokens follow each other; inside a V
- * sub-tile, the 16 token values of one dim are contiguous.  A slot is
+ * i.e. one token's K (or V) for one kv head is one contiguous row of D
+ * elements, so appending a token writes two rows.  A slot is
  * n*bs + t (block n, token t of the block).
  */
 #ifndef PKV_H_

@@ -13,9 +13,9 @@ Names mirror the C ABI in include/pkv.h and include/pkv_alloc.h:
   context_lens, scale, out)`` -- both in one launch (one decode step of one layer)
 * ``BlockAllocator`` -- the host-side block allocator.
 
-Caches are tensors of shape ``(num_blocks, num_kv_heads, block_size // 16, 16 * head_dim)``
-(see ``new_cache``): one row per 16-token sub-tile of a (block, kv head),
-with elements placed as include/pkv.h describes.
+Caches are tensors of shape ``(num_blocks, num_kv_heads, block_size, head_dim)``
+(see ``new_cache``): one contiguous row of ``head_dim`` values per (block, kv
+head, token of the block), K and V alike.
 """
 import ctypes
 import os
@@ -64,14 +64,14 @@ def _device_tensor(t, name, dtype=None, ndim=None):
 def new_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat16, device="cuda"):
     """Uninitialised K or V pool in the library's layout."""
     _need(block_size % 16 == 0, "block_size must be a multiple of 16")
-    return torch.empty((num_blocks, num_kv_heads, block_size // 16, 16 * head_dim), dtype=dtype, device=device)
+    return torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
 
 
 def cache_dims(cache):
     """(num_blocks, num_kv_heads, block_size, head_dim) of a pool made by new_cache."""
-    _need(cache.dim() == 4 and cache.shape[3] % 16 == 0, f"bad cache shape {tuple(cache.shape)}")
-    n, h, s, e = cache.shape
-    return int(n), int(h), int(s) * 16, int(e) // 16
+    _need(cache.dim() == 4 and cache.shape[2] % 16 == 0, f"bad cache shape {tuple(cache.shape)}")
+    n, h, b, d = cache.shape
+    return int(n), int(h), int(b), int(d)
 
 
 def kv_append(k, v, slot_mapping, k_cache, v_cache):

@@ -13,13 +13,19 @@
 //   O^T[D x 16 cols]     += V^T[D x 16 tok] . P^T[16 tok x 16 cols] (D/16 x mfma 16x16x16)
 //
 // The 16 columns are the G q heads that share the kv head (G <= 16; unused
-// columns hold zero queries).  The cache layout makes every operand a plain
-// coalesced load: lane l = 16*kg + r reads the 16-byte K run kg (+4j) of token
-// r -- for fixed j the wave reads one contiguous KB -- and the 8-byte V piece
-// (dim 16j + r, tokens 4kg..4kg+3) -- 512 contiguous bytes per j.  The S tile
-// comes back with lane l holding tokens 4kg..4kg+3 of column r, which is
-// exactly the P^T operand layout of the PV product, so probabilities never
-// leave registers.
+// columns hold zero queries).  The pools are token-major ([bs][D] per block
+// and kv head), so a 16-token sub-tile is 16 consecutive rows of D values.
+// For the K operand lane l = 16*kg + r reads 8 dims (32j + 8kg ..) of token r:
+// 16 bytes, a wave instruction covering half of each of the 16 rows.  The V
+// operand needs 4 tokens of one dim in a lane, across the rows.  The order of
+// the D rows of V^T is free (it only permutes the rows of O^T), so operand j
+// of lane l is taken to be dim JV*r + j (JV = D/16): lane l reads dims
+// JV*r .. JV*r + JV-1 of tokens 4kg + i, i = 0..3 (one load per i; the 16 lanes
+// of a row together read the whole row, so a wave instruction covers 4 full
+// rows), and regroups the 16-bit values in its own registers, with no
+// cross-lane traffic.  The S tile comes back with lane l holding tokens
+// 4kg..4kg+3 of column r, which is exactly the P^T operand layout of the PV
+// product, so probabilities never leave registers.
 //
 // Softmax is online in fp32 (log2 domain).  P enters the PV product rounded to
 // the cache's 16-bit type (round to nearest even); the denominator sums the same
@@ -91,17 +97,43 @@ template <> struct Mma<Fp16> {
 // swizzle); with stride 0 and range 0xffffffff the buffer is a plain byte range.
 constexpr int kBufferConfig = 0x00020000;
 
-// The registers one sub-tile needs: K operands (one per 32 dims) and V
-// operands (one per 16 dims).
+// D/16 16-bit values of one token: the slice of a V row one lane reads.
+template <int D> struct VSlice;
+template <> struct VSlice<64> {
+  u32x2 w;
+  static __device__ __forceinline__ VSlice load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return VSlice{__builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0))};
+  }
+};
+template <> struct VSlice<128> {
+  u32x4 w;
+  static __device__ __forceinline__ VSlice load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    return VSlice{__builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0))};
+  }
+};
+
+// The registers one sub-tile needs: K operands (one per 32 dims) and, for V,
+// the row slices of the lane's 4 tokens.
 template <int D> struct Tile {
   u32x4 k[D / 32];
-  u32x2 v[D / 16];
+  VSlice<D> v[4];
 };
+
+// PV operand j from the 4 row slices: dim JV*r + j of tokens 0..3 as
+// {t0 t1 | t2 t3} (16 bits each, low half first).
+template <int D>
+__device__ __forceinline__ u32x2 v_operand(const VSlice<D> (&v)[4], int j) {
+  const int w = j >> 1;
+  if ((j & 1) == 0)
+    return u32x2{(v[0].w[w] & 0xffffu) | (v[1].w[w] << 16), (v[2].w[w] & 0xffffu) | (v[3].w[w] << 16)};
+  return u32x2{(v[0].w[w] >> 16) | (v[1].w[w] & 0xffff0000u), (v[2].w[w] >> 16) | (v[3].w[w] & 0xffff0000u)};
+}
 
 // Fused append, store side: the same bytes kv_append writes for token i =
 // sequence i, after the checks the decode side makes (a valid length, and the
 // slot is the slot of position L_i - 1); thread per (token, kv head, 8-dim run)
-// as in kv_append, grid-strided over the append workgroups.
+// as in kv_append, grid-strided over the append workgroups.  A token's K and V
+// are one D-value row each.
 template <int D, int NT>
 __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
   constexpr int runs = D / 8;
@@ -122,17 +154,9 @@ __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
     if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
         slot != static_cast<int64_t>(phys) * p.block_size + off)
       continue;
-    const size_t sub = (static_cast<size_t>(phys) * p.num_kv_heads + h) * (p.block_size >> 4) + (off >> 4);
-    const int r = off & 15;
-    const u32x4 kk = *reinterpret_cast<const u32x4*>(p.k_new + th * D + c * 8);
-    const u32x4 vv = *reinterpret_cast<const u32x4*>(p.v_new + th * D + c * 8);
-    *reinterpret_cast<u32x4*>(p.k_cache_w + ((sub * runs + c) * 16 + r) * 8) = kk;
-    uint16_t* vb = p.v_cache_w + (sub * D + c * 8) * 16 + r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vb[(2 * e) * 16] = static_cast<uint16_t>(vv[e] & 0xffffu);
-      vb[(2 * e + 1) * 16] = static_cast<uint16_t>(vv[e] >> 16);
-    }
+    const size_t row = ((static_cast<size_t>(phys) * p.num_kv_heads + h) * p.block_size + off) * D + c * 8;
+    *reinterpret_cast<u32x4*>(p.k_cache_w + row) = *reinterpret_cast<const u32x4*>(p.k_new + th * D + c * 8);
+    *reinterpret_cast<u32x4*>(p.v_cache_w + row) = *reinterpret_cast<const u32x4*>(p.v_new + th * D + c * 8);
   }
 }
 
@@ -252,8 +276,8 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
   // Buffer loads: the sub-tile's base address lives in a wave-uniform
   // resource (scalar registers) and each lane keeps two constant byte
   // offsets, so no per-load address occupies vector registers.
-  const int koff = ((kg * 16) + r) * 16;     // K run kg of token r; + 1 KB (scalar offset) per j
-  const int voff = r * 32 + kg * 8;          // V dim r, tokens 4kg..4kg+3; + 512 B per j
+  const int koff = (r * D + kg * 8) * 2;        // K token r, dims 8kg..; + 64 B (scalar offset) per j
+  const int voff = (4 * kg * D + r * JV) * 2;   // V token 4kg, dims JV*r..; + one row (scalar offset) per token
   auto load = [&](int k, Tile<D>& t) {
     int sub = __builtin_amdgcn_readlane(tid, k);
     bad |= sub < 0;
@@ -264,10 +288,9 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vt), 0, -1, kBufferConfig);
 #pragma unroll
     for (int j = 0; j < JK; ++j)
-      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 1024 * j, 0));
+      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 64 * j, 0));
 #pragma unroll
-    for (int j = 0; j < JV; ++j)
-      t.v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 512 * j, 0));
+    for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
   };
 
   float m = -INFINITY, l = 0.f;
@@ -284,17 +307,15 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
 #pragma unroll
         for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(&sm_new[0][(4 * j + kg) * 8]);
       }
-      if (kg == (app_r >> 2)) {
-        const int sh = (app_r & 1) * 16;
-        const uint32_t keep = ~(0xffffu << sh);
+      if ((app_r >> 2) == kg) {
 #pragma unroll
-        for (int j = 0; j < JV; ++j) {
-          const uint32_t v = static_cast<uint32_t>(sm_new[1][16 * j + r]) << sh;
-          if (app_r & 2) t.v[j].y = (t.v[j].y & keep) | v;
-          else t.v[j].x = (t.v[j].x & keep) | v;
-        }
+        for (int i = 0; i < 4; ++i)
+          if ((app_r & 3) == i) t.v[i] = *reinterpret_cast<const VSlice<D>*>(&sm_new[1][r * JV]);
       }
     }
+    u32x2 vop[JV];
+#pragma unroll
+    for (int j = 0; j < JV; ++j) vop[j] = v_operand<D>(t.v, j);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[j], sc);
@@ -319,13 +340,13 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
       const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
       for (int j = 0; j < JV; ++j) {
-        t.v[j].x &= m0;
-        t.v[j].y &= m1;
+        vop[j].x &= m0;
+        vop[j].y &= m1;
       }
     }
     const u32x2 pop = {p01, p23};
 #pragma unroll
-    for (int j = 0; j < JV; ++j) o[j] = Mma<T>::pv(t.v[j], pop, o[j]);
+    for (int j = 0; j < JV; ++j) o[j] = Mma<T>::pv(vop[j], pop, o[j]);
   };
 
   // S register slots; slot i holds sub-tiles i, i+S, i+2S, ...  Steps past
@@ -361,7 +382,7 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
 #pragma unroll
     for (int j = 0; j < JV; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm_o[wv][r][16 * j + 4 * kg + i] = o[j][i];
+      for (int i = 0; i < 4; ++i) sm_o[wv][r][(4 * kg + i) * JV + j] = o[j][i];  // row 4kg+i of O^T is that dim
   }
   __syncthreads();
   combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1);

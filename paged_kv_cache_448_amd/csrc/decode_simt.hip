@@ -7,13 +7,15 @@
 // 2~4배 끌어올린 서빙 엔진", section "PagedAttention -- OS 가상 메모리에서 영감").
 //
 // One workgroup = one (sequence, kv head, partition of the context), NW waves.
-// The waves take the partition's 16-token sub-tiles round robin.  Per sub-tile
-// a wave holds, lane l = 16*kg + tt:
+// The waves take the partition's 16-token sub-tiles round robin (the pools are
+// token-major, so a sub-tile is 16 rows of D values).  Per sub-tile a wave
+// holds, lane l = 16*kg + tt:
 //   * K: token tt, dims of 8-dim runs kg, kg+4, ... (D/32 runs of 16 bytes);
 //     the partial dot products with the G queries are summed over kg by two
 //     cross-row shuffles, so every lane ends with the score of token tt;
-//   * V: dim l (and l+64 for D=128), all 16 tokens (two 16-byte loads);
-//     the probabilities of the 16 tokens are broadcast with readlane.
+//   * V: dim l (and l+64 for D=128) of all 16 tokens (16 two-byte loads, each
+//     instruction one row); the probabilities of the 16 tokens are broadcast
+//     with readlane.
 // Softmax is online in fp32 (log2 domain, scale folded into the score).
 // Tokens past the context are masked by select: their score becomes -inf and
 // their V values 0, so NaN in tail slots never reaches the output.
@@ -87,14 +89,13 @@ __global__ __launch_bounds__(NW * kWave) void decode_simt_kernel(DecodeParams p)
     const uint16_t* vt = p.v_cache + tile * (16 * D);
     uint4 kr[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) kr[j] = *reinterpret_cast<const uint4*>(kt + ((kg + 4 * j) * 16 + tt) * 8);
-    uint4 vr[DV][2];
+    for (int j = 0; j < J; ++j) kr[j] = *reinterpret_cast<const uint4*>(kt + tt * D + (kg + 4 * j) * 8);
+    // V: lane l holds dim l (and l + 64) of the 16 tokens; each load is one row
+    uint16_t vr[DV][16];
 #pragma unroll
-    for (int e = 0; e < DV; ++e) {
-      const uint4* vp = reinterpret_cast<const uint4*>(vt + (lane + 64 * e) * 16);
-      vr[e][0] = vp[0];
-      vr[e][1] = vp[1];
-    }
+    for (int e = 0; e < DV; ++e)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) vr[e][t] = vt[t * D + lane + 64 * e];
     const int nvalid = min(16, end - tok0);
     const bool valid = tt < nvalid;
 
@@ -126,10 +127,9 @@ __global__ __launch_bounds__(NW * kWave) void decode_simt_kernel(DecodeParams p)
 
     float vv[DV][16];
 #pragma unroll
-    for (int e = 0; e < DV; ++e) {
-      unpack8<T>(vr[e][0], vv[e]);
-      unpack8<T>(vr[e][1], vv[e] + 8);
-    }
+    for (int e = 0; e < DV; ++e)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) vv[e][t] = lo_f32<T>(vr[e][t]);
     if (nvalid < 16) {
 #pragma unroll
       for (int e = 0; e < DV; ++e)

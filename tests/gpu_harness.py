@@ -49,7 +49,7 @@ class DevWorkload:
 
 def cache_shape(wl):
     c = wl.cfg
-    return (wl.num_blocks, c.num_kv_heads, c.block_size // 16, 16 * c.head_dim)
+    return (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
 
 
 def upload(wl, layers=None):

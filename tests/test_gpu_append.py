@@ -53,7 +53,7 @@ def test_append_many_tokens_random_slots(Hkv, D, bs, dtype):
     v = workloads.random_bits(rng, (T, Hkv, D), dtype)
     kc = workloads.random_bits(rng, (N * Hkv * bs * D,), dtype)
     vc = workloads.random_bits(rng, (N * Hkv * bs * D,), dtype)
-    shape = (N, Hkv, bs // 16, 16 * D)
+    shape = (N, Hkv, bs, D)
     dk, dv = to_dev(kc, dtype, shape), to_dev(vc, dtype, shape)
     pkv.kv_append(to_dev(k, dtype), to_dev(v, dtype), torch.from_numpy(slots).cuda(), dk, dv)
     keep = slots < total

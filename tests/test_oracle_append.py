@@ -27,15 +27,15 @@ def test_offset_formula_matches_view(Hkv, bs, D):
     assert np.array_equal(layout.v_logical(vflat, N, Hkv, bs, D), logical_index)
 
 
-def test_k_subtile_is_16_byte_runs():
-    """Inside a 16-token sub-tile, 8 consecutive dims of one token are contiguous, and
-    the same 8 dims of consecutive tokens follow each other."""
-    assert layout.k_offset(0, 0, 0, 1, 1, 16, 64) == 1
-    assert layout.k_offset(0, 0, 1, 0, 1, 16, 64) == 8
-    assert layout.k_offset(0, 0, 0, 8, 1, 16, 64) == 128
-    assert layout.v_offset(0, 0, 1, 0, 1, 16, 64) == 1
-    assert layout.v_offset(0, 0, 0, 1, 1, 16, 64) == 16
-    assert layout.k_offset(1, 0, 0, 0, 2, 16, 64) == 2 * 16 * 64
+def test_token_rows_are_contiguous():
+    """K and V alike: one token's D values for one kv head are one contiguous row; rows of a
+    block's tokens follow each other, then the next kv head, then the next block."""
+    for off in (layout.k_offset, layout.v_offset):
+        assert off(0, 0, 0, 1, 1, 16, 64) == 1
+        assert off(0, 0, 1, 0, 1, 16, 64) == 64
+        assert off(0, 1, 0, 0, 2, 16, 64) == 16 * 64
+        assert off(1, 0, 0, 0, 2, 16, 64) == 2 * 16 * 64
+        assert off(2, 1, 15, 63, 2, 16, 64) == ((2 * 2 + 1) * 16 + 15) * 64 + 63
 
 
 def _case():

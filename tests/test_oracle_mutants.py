@@ -49,9 +49,8 @@ def _no_max_attend(q_heads, k_ctx, v_ctx, scale64):
     return (w @ v_ctx) / w.sum(axis=1, keepdims=True)
 
 
-def _transposed_k_view(k_flat, N, Hkv, bs, D):
-    a = k_flat.reshape(N, Hkv, bs // 16, D // 8, 16, 8)
-    return a.reshape(N, Hkv, bs, D)                # forgets the transpose
+def _token_major_k_view(k_flat, N, Hkv, bs, D):
+    return k_flat.reshape(N, bs, Hkv, D).transpose(0, 2, 1, 3)   # tokens outside kv heads
 
 
 MUTANTS = {
@@ -62,7 +61,7 @@ MUTANTS = {
     "gather-wrong-offset": lambda mp: mp.setattr(att, "gather_context", _wrong_offset_gather),
     "k-v-swapped": lambda mp: mp.setattr(att, "gather_context", _swapped_kv_gather(att.gather_context)),
     "softmax-without-max": lambda mp: mp.setattr(att, "attend", _no_max_attend),
-    "k-layout-untransposed": lambda mp: mp.setattr(att, "k_logical", _transposed_k_view),
+    "k-layout-heads-and-tokens-swapped": lambda mp: mp.setattr(att, "k_logical", _token_major_k_view),
 }
 
 
