@@ -202,8 +202,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the decode path has no multi-GPU mode in this build "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path has no multi-GPU mode (each GPU would run "
+              "its own sequences or kv heads on its own pools); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import workloads
