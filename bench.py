@@ -34,6 +34,12 @@ Other modes (measurement tooling):
                       (FETCH_SIZE, then WRITE_SIZE) into the traffic summary
                       under profiles/ that later runs report as
                       roofline.traffic while the decode sources are unchanged.
+  --loop NAME         continuous-batching loop instead of one batch: requests
+                      are admitted (prompt K/V written), decode one token per
+                      step over all layers, and leave, for W + K steps of a
+                      seeded plan (workloads.loop); reports sustained decode
+                      tokens/s over the K timed steps, host scheduling, copies
+                      and prompt writes included.  Its own JSON line.
 """
 import argparse
 import hashlib
@@ -184,6 +190,81 @@ def load_traffic(workload_name):
     return rec["traffic_bytes_per_launch"]
 
 
+def loop_bench(name, steps, warmup, seed=11):
+    """Sustained decode tokens/s of the continuous-batching loop (see --loop)."""
+    import torch
+
+    from paged_kv_cache_448_amd.loop import DecodeLoop
+    from workloads import loop as wl_loop
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    lc = wl_loop.LOOP_CONFIGS[name]
+    reqs, plan = wl_loop.plan(lc, seed, warmup + steps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    most_prompt = max(sum(reqs[r].prompt_len for r in st.admit) for st in plan)
+    loop = DecodeLoop(lc, dev, max_prompt_tokens=most_prompt)
+    tdt = loop.dtype
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    B = lc.max_batch
+    # values do not change the work, so every step reuses one set of them
+    q = torch.randn((B, lc.num_q_heads, lc.head_dim), generator=g, device=dev).to(tdt)
+    kn = torch.randn((B, lc.num_kv_heads, lc.head_dim), generator=g, device=dev).to(tdt)
+    vn = torch.randn((B, lc.num_kv_heads, lc.head_dim), generator=g, device=dev).to(tdt)
+    kp = torch.randn((most_prompt, lc.num_kv_heads, lc.head_dim), generator=g, device=dev).to(tdt)
+    vp = torch.randn((most_prompt, lc.num_kv_heads, lc.head_dim), generator=g, device=dev).to(tdt)
+    outs = [torch.empty((B, lc.num_q_heads, lc.head_dim), dtype=tdt, device=dev) for _ in range(lc.num_layers)]
+    per_token_kv = 2 * lc.num_kv_heads * lc.head_dim * 2
+
+    def run(st):
+        if st.admit:
+            lens_p = [reqs[rid].prompt_len for rid in st.admit]
+            T = sum(lens_p)
+            loop.admit(st.admit, lens_p, lambda layer: (kp[:T], vp[:T]))
+        n = len(st.run)
+        lens = loop.decode_step(st.run, lambda layer: (q[:n], kn[:n], vn[:n]), [o[:n] for o in outs])
+        for rid in st.finish:
+            loop.finish(rid)
+        return n, int(np.asarray(lens, dtype=np.int64).sum()), sum(reqs[r].prompt_len for r in st.admit)
+
+    for st in plan[:warmup]:
+        run(st)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tokens = ctx_tokens = prompt_tokens = 0
+    loop.host_wait_s = 0.0
+    h0 = time.perf_counter()
+    e0.record(stream)
+    for st in plan[warmup:]:
+        n, c, pt = run(st)
+        tokens += n
+        ctx_tokens += c
+        prompt_tokens += pt
+    e1.record(stream)
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    gpu_ms = e0.elapsed_time(e1)
+    wall_s = max(gpu_ms / 1e3, host_s)
+    kv_bytes = ctx_tokens * per_token_kv * lc.num_layers
+    log(f"loop {name}: {steps} steps, {tokens} decode tokens (batch {tokens / steps:.1f} on average), "
+        f"{prompt_tokens} prompt tokens written; GPU {gpu_ms:.2f} ms, host enqueue {host_s * 1e3:.2f} ms "
+        f"(of which {loop.host_wait_s * 1e3:.2f} ms waiting for the GPU); "
+        f"{kv_bytes / 1e9:.2f} GB of context K/V read")
+    rec = {"metric": "continuous-batching decode tokens/s", "value": round(tokens / wall_s, 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(wall_s * 1e3 / steps, 4),
+           "higher_is_better": True, "dtype": lc.dtype, "data": "synthetic",
+           "config": {"workload": f"{name}: {lc.num_layers} layers, {lc.num_q_heads}q/{lc.num_kv_heads}kv heads, "
+                                  f"head_dim {lc.head_dim}, block_size {lc.block_size}, batch up to {lc.max_batch}, "
+                                  f"seed {seed}"},
+           "avg_batch": round(tokens / steps, 2), "gpu_ms": round(gpu_ms, 3), "host_enqueue_ms": round(host_s * 1e3, 3),
+           "host_wait_ms": round(loop.host_wait_s * 1e3, 3),
+           "kv_read_gbs": round(kv_bytes / (wall_s * 1e9), 1),
+           "kv_read_frac_of_peak": round(kv_bytes / (wall_s * 1e9) / HBM_PEAK_GBS, 4)}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,12 +280,17 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture the K timed steps into one HIP graph and replay it (fused path only)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--loop", default=None, help="continuous-batching loop workload (e.g. cb-llama3.2-1b)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the decode path has no multi-GPU mode (each GPU would run "
               "its own sequences or kv heads on its own pools); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.loop:
+        loop_bench(args.loop, args.steps, args.warmup)
+        return
 
     import workloads
     if args.pmc_summary:

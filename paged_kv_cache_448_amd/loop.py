@@ -1,0 +1,183 @@
+"""Continuous-batching decode loop: the host block allocator driving the library's kernels.
+
+Each step of a plan (requests admitted, sequences decoding, sequences leaving;
+see workloads.loop for the plans used in tests and benchmarks):
+
+1. the admitted requests take the blocks of their prompts from the host
+   allocator, and their prompt K/V is written into each layer's pool (one
+   kv_append per layer for all of them, one slot per prompt token);
+2. every running sequence takes the slot of its next token (append_slots: a
+   fresh block whenever the last one is full), and the running batch's block
+   tables, context lengths and slots are copied to the device;
+3. each layer runs one fused append + decode launch;
+4. sequences that are done return their blocks to the pool.  Their blocks may
+   be handed out again in the next step; the stream orders the next step's
+   writes after this step's reads.
+
+Host arrays go through a small ring of pinned buffers so the host can prepare
+the next steps while the GPU runs the current one.  The per-step launches call
+the C ABI directly with pointers checked once at construction (the pools, the
+staging buffers) or by shape (the caller's q/k/v/out), because at hundreds of
+sequences and 16 layers a step's host time is otherwise dominated by argument
+checking.  Everything on the device path is the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import time
+
+import numpy as np
+import torch
+
+from . import PKV_BF16, PKV_FP16, check, decode_workspace_bytes, lib, new_cache
+from ._lib import PkvError
+from .allocator import BlockAllocator
+
+_TORCH_DTYPES = {"bf16": torch.bfloat16, "fp16": torch.float16}
+_DTYPE_CODES = {"bf16": PKV_BF16, "fp16": PKV_FP16}
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class DecodeLoop:
+    """Pools for every layer, the host allocator, and the per-step staging."""
+
+    def __init__(self, lc, device="cuda", shuffle_seed: int = 1, ring: int = 4, max_prompt_tokens: int = 0):
+        self.lc = lc
+        self.device = torch.device(device)
+        self.dtype = _TORCH_DTYPES[lc.dtype]
+        self.code = _DTYPE_CODES[lc.dtype]
+        self.alloc = BlockAllocator(lc.num_blocks, lc.block_size, shuffle_seed)
+        self.k_pools = [new_cache(lc.num_blocks, lc.num_kv_heads, lc.block_size, lc.head_dim, self.dtype, self.device)
+                        for _ in range(lc.num_layers)]
+        self.v_pools = [new_cache(lc.num_blocks, lc.num_kv_heads, lc.block_size, lc.head_dim, self.dtype, self.device)
+                        for _ in range(lc.num_layers)]
+        self.max_blocks = math.ceil(lc.max_context / lc.block_size)
+        # prompt tokens one step may admit (default: a full batch of the longest prompts)
+        self.max_prompt_tokens = max_prompt_tokens if max_prompt_tokens > 0 else lc.max_batch * lc.prompt_hi
+        B = lc.max_batch
+        ws = decode_workspace_bytes(B, lc.num_q_heads, lc.num_kv_heads, lc.head_dim, lc.block_size, lc.max_context)
+        self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
+        self.tables_d = torch.empty(B * self.max_blocks, dtype=torch.int32, device=self.device)
+        self.lens_d = torch.empty(B, dtype=torch.int32, device=self.device)
+        self.slots_d = torch.empty(B, dtype=torch.int64, device=self.device)
+        self.prompt_slots_d = torch.empty(self.max_prompt_tokens, dtype=torch.int64, device=self.device)
+        pin = dict(pin_memory=True)
+        self._ring = [dict(tables=torch.empty(B * self.max_blocks, dtype=torch.int32, **pin),
+                           lens=torch.empty(B, dtype=torch.int32, **pin),
+                           slots=torch.empty(B, dtype=torch.int64, **pin),
+                           pslots=torch.empty(self.max_prompt_tokens, dtype=torch.int64, **pin),
+                           done=None) for _ in range(ring)]
+        self._next = 0
+        self._lib = lib()
+        self.host_wait_s = 0.0  # time the host spent waiting for the GPU to free a staging buffer
+
+    def _staging(self):
+        st = self._ring[self._next]
+        self._next = (self._next + 1) % len(self._ring)
+        if st["done"] is not None:
+            t0 = time.perf_counter()
+            st["done"].synchronize()  # the copies out of this buffer have run
+            self.host_wait_s += time.perf_counter() - t0
+        return st
+
+    def _release(self, st, stream):
+        ev = torch.cuda.Event()
+        ev.record(stream)
+        st["done"] = ev
+
+    def _check(self, t, shape, name):
+        if not (t.is_cuda and t.dtype == self.dtype and t.is_contiguous() and tuple(t.shape) == shape):
+            raise PkvError(f"{name} must be a contiguous {self.dtype} GPU tensor of shape {shape}, got "
+                           f"{t.dtype} {tuple(t.shape)}")
+
+    def admit(self, rids, prompt_lens, prompt_kv):
+        """Register requests rids with their prompt lengths and write their prompts' K/V.
+
+        prompt_kv(layer) -> (k, v): device tensors [sum(prompt_lens), Hkv, D], the
+        prompts one after the other in the order of rids."""
+        lc, bs = self.lc, self.lc.block_size
+        slots = []
+        for rid, P in zip(rids, prompt_lens):
+            self.alloc.add_seq(int(rid), int(P))
+            if P:
+                table, _ = self.alloc.block_tables([int(rid)], -(-int(P) // bs))
+                pos = np.arange(int(P), dtype=np.int64)
+                slots.append(table[0, pos // bs].astype(np.int64) * bs + pos % bs)
+        T = int(sum(len(s) for s in slots))
+        if T == 0:
+            return
+        if T > self.max_prompt_tokens:
+            raise PkvError(f"{T} prompt tokens in one step; the loop stages at most {self.max_prompt_tokens}")
+        stream = torch.cuda.current_stream(self.device)
+        st = self._staging()
+        st["pslots"][:T].numpy()[:] = np.concatenate(slots)
+        self.prompt_slots_d[:T].copy_(st["pslots"][:T], non_blocking=True)
+        self._release(st, stream)
+        shape = (T, lc.num_kv_heads, lc.head_dim)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        for layer in range(lc.num_layers):
+            k, v = prompt_kv(layer)
+            self._check(k, shape, "prompt k")
+            self._check(v, shape, "prompt v")
+            check(self._lib.pkv_kv_append(_p(k), _p(v), _p(self.prompt_slots_d), T, _p(self.k_pools[layer]),
+                                          _p(self.v_pools[layer]), lc.num_blocks, bs, lc.num_kv_heads, lc.head_dim,
+                                          self.code, sp))
+
+    def decode_step(self, run_ids, step_qkv, outs):
+        """One token for every sequence in run_ids (batch order).
+
+        step_qkv(layer) -> (q [B, Hq, D], k [B, Hkv, D], v [B, Hkv, D]) device tensors;
+        outs[layer]: [B, Hq, D] output tensors.  Returns the batch's context lengths."""
+        lc, bs = self.lc, self.lc.block_size
+        B = len(run_ids)
+        if B == 0:
+            return np.zeros(0, dtype=np.int32)
+        if B > lc.max_batch:
+            raise PkvError(f"batch of {B} exceeds the loop's max_batch {lc.max_batch}")
+        slots = self.alloc.append_slots(run_ids)
+        tables, lens = self.alloc.block_tables(run_ids, self.max_blocks, pad_value=0)
+        lens_max = int(lens.max())
+        M = -(-lens_max // bs)  # only the columns the batch uses go to the device
+        stream = torch.cuda.current_stream(self.device)
+        st = self._staging()
+        st["tables"][:B * M].numpy().reshape(B, M)[:] = tables[:, :M]
+        st["lens"][:B].numpy()[:] = lens
+        st["slots"][:B].numpy()[:] = slots
+        self.tables_d[:B * M].copy_(st["tables"][:B * M], non_blocking=True)
+        self.lens_d[:B].copy_(st["lens"][:B], non_blocking=True)
+        self.slots_d[:B].copy_(st["slots"][:B], non_blocking=True)
+        self._release(st, stream)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        qs, kvs = (B, lc.num_q_heads, lc.head_dim), (B, lc.num_kv_heads, lc.head_dim)
+        ws = ctypes.c_size_t(self.workspace.numel())
+        scale = ctypes.c_float(lc.scale)
+        for layer in range(lc.num_layers):
+            q, k, v = step_qkv(layer)
+            out = outs[layer]
+            self._check(q, qs, "q")
+            self._check(k, kvs, "k")
+            self._check(v, kvs, "v")
+            self._check(out, qs, "out")
+            check(self._lib.pkv_append_paged_attn_decode(
+                _p(q), _p(k), _p(v), _p(self.slots_d), _p(self.k_pools[layer]), _p(self.v_pools[layer]),
+                _p(self.tables_d), M, _p(self.lens_d), lens_max, scale, _p(out), B, lc.num_q_heads, lc.num_kv_heads,
+                lc.head_dim, bs, lc.num_blocks, self.code, _p(self.workspace), ws, 0, sp))
+        return lens
+
+    def finish(self, rid: int):
+        self.alloc.free_seq(int(rid))
+
+    def gather(self, rid: int, layer: int):
+        """K and V of sequence rid in one layer, in token order, as device tensors [L, Hkv, D] (for checks)."""
+        L = self.alloc.context_len(rid)
+        bs = self.lc.block_size
+        table, _ = self.alloc.block_tables([rid], max(1, -(-L // bs)))
+        pos = torch.arange(L, device=self.device)
+        blk = torch.from_numpy(table[0].astype(np.int64)).to(self.device)[pos // bs]
+        k = self.k_pools[layer][blk, :, pos % bs, :]
+        v = self.v_pools[layer][blk, :, pos % bs, :]
+        return k, v
