@@ -221,7 +221,7 @@ def loop_bench(name, steps, warmup, seed=11):
         if st.admit:
             lens_p = [reqs[rid].prompt_len for rid in st.admit]
             T = sum(lens_p)
-            loop.admit(st.admit, lens_p, lambda layer: (kp[:T], vp[:T]))
+            loop.admit(st.admit, lens_p, lambda layer, cached: (kp[:T], vp[:T]))
         n = len(st.run)
         lens = loop.decode_step(st.run, lambda layer: (q[:n], kn[:n], vn[:n]), [o[:n] for o in outs])
         for rid in st.finish:

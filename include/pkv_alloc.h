@@ -55,6 +55,21 @@ int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq_id, int32_t num_tokens);
 int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t src_seq,
                              int32_t num_shared_blocks);
 
+/* Register seq_id with a num_tokens-token prompt given by its token ids, and
+ * share the longest run of leading full blocks that a live sequence already
+ * holds for the same tokens (prefix caching, "Nano-vLLM로 배우는 vLLM 추론 엔진
+ * 작동 원리 한눈에 정리", section "KV 캐시와 Block Manager": a full block is
+ * identified by a hash chained over its tokens and all earlier blocks' tokens;
+ * a match is confirmed token by token and parent block by parent block).
+ * *cached_tokens_out receives the number of leading tokens (a multiple of
+ * block_size) whose K/V those shared blocks already hold: the caller writes K/V
+ * only for the tokens after them.  The new sequence's own full blocks are
+ * registered for later prompts; a block leaves the registry when its last
+ * holder frees it.  Only prompt blocks are registered (tokens appended later
+ * are not known here).  PKV_E_NULL, PKV_E_EXISTS, PKV_E_NOMEM, PKV_E_SHAPE. */
+int pkv_alloc_add_seq_prefix(pkv_alloc* a, int64_t seq_id, const int32_t* token_ids, int32_t num_tokens,
+                             int32_t* cached_tokens_out);
+
 /* Grow seq_id by one token; *slot_out receives that token's slot
  * (block * block_size + offset).  Takes a fresh block when the last one is full.
  * PKV_E_NOSEQ, PKV_E_NOMEM (the caller's cue to preempt or wait). */

@@ -11,7 +11,8 @@ Many assignments are correct, so this checks properties, not block ids:
 * entries [0, ceil(L_i/bs)) of row i are valid block ids, the rest are padding;
 * a physical block appears in at most one (sequence, logical index) place,
   unless it is declared shared, and then every use is at the same logical index
-  and is a full block lying before the sequence's last token;
+  and is a full block lying before the position the sequence writes next (so an
+  append never writes into a shared block);
 * the number of free blocks is N minus the distinct blocks in use;
 * the slot of position p of sequence i is table[i, p // bs] * bs + p % bs.
 """
@@ -22,7 +23,10 @@ def blocks_needed(length: int, block_size: int) -> int:
     return -(-int(length) // block_size)
 
 
-def check_tables(tables, lens, *, num_blocks, block_size, pad_value, shared=()):
+def check_tables(tables, lens, *, num_blocks, block_size, pad_value, shared=(), appended=True):
+    """appended: the lengths count a token appended this step (position L-1 was just
+    written, so a shared block must end before it); False: the state right after a
+    prompt is registered, whose next write is position L (a shared block must be full)."""
     tables = np.asarray(tables)
     lens = np.asarray(lens)
     shared = set(int(x) for x in shared)
@@ -39,7 +43,8 @@ def check_tables(tables, lens, *, num_blocks, block_size, pad_value, shared=()):
                 assert seen[p] == j, f"shared block {p} at different logical indices"
             seen[p] = j
             if p in shared:
-                assert block_size * (j + 1) <= lens[i] - 1, f"seq {i}: shared block {p} not full before the last token"
+                last = lens[i] - 1 if appended else lens[i]
+                assert block_size * (j + 1) <= last, f"seq {i}: shared block {p} not full before the next write"
         assert np.all(row[nb:] == pad_value), f"seq {i}: padding entries wrong"
     return len(seen)
 

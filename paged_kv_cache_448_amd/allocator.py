@@ -38,6 +38,16 @@ class BlockAllocator:
         check(lib().pkv_alloc_add_seq_shared(self._h, int(seq_id), int(num_tokens), int(src_seq),
                                              int(num_shared_blocks)))
 
+    def add_seq_prefix(self, seq_id: int, token_ids) -> int:
+        """Register seq_id with its prompt's token ids, sharing the leading full blocks a live
+        sequence already holds for the same tokens; returns how many leading tokens' K/V are
+        already in the pool (the caller writes K/V only for the rest)."""
+        ids = np.ascontiguousarray(token_ids, dtype=np.int32)
+        out = ctypes.c_int32()
+        check(lib().pkv_alloc_add_seq_prefix(self._h, int(seq_id), ids.ctypes.data if len(ids) else None, len(ids),
+                                             ctypes.byref(out)))
+        return out.value
+
     def append_slot(self, seq_id: int) -> int:
         out = ctypes.c_int64()
         check(lib().pkv_alloc_append_slot(self._h, int(seq_id), ctypes.byref(out)))

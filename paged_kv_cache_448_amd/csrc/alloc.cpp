@@ -7,7 +7,15 @@
 // blocks taken only as tokens arrive, non-contiguous physical blocks behind a
 // contiguous logical sequence, free blocks reusable by any request) and the
 // Nano-vLLM page ("Nano-vLLM로 배우는 vLLM 추론 엔진 작동 원리 한눈에 정리",
-// section "KV 캐시와 Block Manager": metadata on the CPU, shared prefix blocks).
+// section "KV 캐시와 Block Manager": metadata on the CPU, shared prefix blocks
+// found by hashing the blocks' tokens).
+//
+// Prefix caching: a full prompt block is registered under a hash chained over
+// its tokens and every earlier block's, so a later prompt that starts with the
+// same full blocks of tokens finds them and shares them.  A match is confirmed
+// exactly (same tokens, same parent block), so a hash collision can never
+// share the wrong block.  A block leaves the registry when its last holder
+// frees it.
 #include "pkv_alloc.h"
 
 #include <algorithm>
@@ -25,6 +33,12 @@ struct pkv_alloc {
   std::vector<int32_t> free_stack;  // next block handed out is free_stack.back()
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
+  // prefix registry: chained hash -> block; per block its hash (0: not
+  // registered), parent block (-1: first block of a prompt) and tokens
+  std::unordered_map<uint64_t, int32_t> by_hash;
+  std::vector<uint64_t> block_hash;
+  std::vector<int32_t> block_parent;
+  std::vector<int32_t> block_tokens;
 
   int32_t take() {
     const int32_t b = free_stack.back();
@@ -33,7 +47,14 @@ struct pkv_alloc {
     return b;
   }
   void release(int32_t b) {
-    if (--refcount[b] == 0) free_stack.push_back(b);
+    if (--refcount[b] == 0) {
+      if (block_hash[b] != 0) {
+        auto it = by_hash.find(block_hash[b]);
+        if (it != by_hash.end() && it->second == b) by_hash.erase(it);
+        block_hash[b] = 0;
+      }
+      free_stack.push_back(b);
+    }
   }
   int32_t blocks_for(int64_t tokens) const {
     return static_cast<int32_t>((tokens + block_size - 1) / block_size);
@@ -51,6 +72,23 @@ uint64_t splitmix64(uint64_t& state) {
   return z ^ (z >> 31);
 }
 
+// FNV-1a over the 32-bit tokens of one block, continuing from the previous
+// block's hash (Fowler, Noll, Vo; 64-bit offset basis replaced by the chain
+// value), then a SplitMix64 finaliser; never 0 (0 marks an unregistered block).
+uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int32_t n) {
+  uint64_t h = prev ^ 0xcbf29ce484222325ull;
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t t = static_cast<uint32_t>(tokens[i]);
+    for (int k = 0; k < 4; ++k) {
+      h ^= (t >> (8 * k)) & 0xffu;
+      h *= 0x100000001b3ull;
+    }
+  }
+  uint64_t s = h;
+  const uint64_t z = splitmix64(s);
+  return z == 0 ? 1 : z;
+}
+
 }  // namespace
 
 extern "C" {
@@ -63,6 +101,8 @@ pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, uint64_t shu
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->refcount.assign(num_blocks, 0);
+    a->block_hash.assign(num_blocks, 0);
+    a->block_parent.assign(num_blocks, -1);
     // hand-out order: order[0] first
     std::vector<int32_t> order(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
@@ -119,6 +159,65 @@ int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, i
   }
   for (int32_t j = 0; j < fresh; ++j) s.blocks.push_back(a->take());
   a->seqs.emplace(seq_id, std::move(s));
+  return PKV_OK;
+}
+
+int pkv_alloc_add_seq_prefix(pkv_alloc* a, int64_t seq_id, const int32_t* token_ids, int32_t num_tokens,
+                             int32_t* cached_tokens_out) {
+  if (!a || !cached_tokens_out || (num_tokens > 0 && !token_ids)) return PKV_E_NULL;
+  if (num_tokens < 0) return PKV_E_SHAPE;
+  if (a->seqs.count(seq_id)) return PKV_E_EXISTS;
+  const int32_t bs = a->block_size;
+  const int32_t need = a->blocks_for(num_tokens), full = num_tokens / bs;
+  // longest run of leading full blocks already registered (exact match)
+  std::vector<uint64_t> hashes(full);
+  int32_t shared = 0, parent = -1;
+  uint64_t h = 0x6a09e667f3bcc909ull;
+  for (int32_t j = 0; j < full; ++j) {
+    h = chain_hash(h, token_ids + static_cast<int64_t>(j) * bs, bs);
+    hashes[j] = h;
+    if (shared == j) {
+      auto it = a->by_hash.find(h);
+      if (it != a->by_hash.end() && a->block_parent[it->second] == parent &&
+          std::equal(token_ids + static_cast<int64_t>(j) * bs, token_ids + static_cast<int64_t>(j + 1) * bs,
+                     a->block_tokens.begin() + static_cast<int64_t>(it->second) * bs)) {
+        parent = it->second;
+        ++shared;
+      }
+    }
+  }
+  if (need - shared > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  try {
+    if (a->block_tokens.empty()) a->block_tokens.assign(static_cast<size_t>(a->num_blocks) * bs, 0);
+    pkv_alloc::Seq s;
+    s.len = num_tokens;
+    s.blocks.reserve(need);
+    parent = -1;
+    for (int32_t j = 0; j < need; ++j) {
+      int32_t b;
+      if (j < shared) {
+        b = a->by_hash.find(hashes[j])->second;
+        ++a->refcount[b];
+      } else {
+        b = a->take();
+        if (j < full && a->by_hash.find(hashes[j]) == a->by_hash.end()) {
+          // register the new full block (a block already registered under this
+          // hash stays the one later prompts find)
+          a->by_hash.emplace(hashes[j], b);
+          a->block_hash[b] = hashes[j];
+          a->block_parent[b] = parent;
+          std::copy(token_ids + static_cast<int64_t>(j) * bs, token_ids + static_cast<int64_t>(j + 1) * bs,
+                    a->block_tokens.begin() + static_cast<int64_t>(b) * bs);
+        }
+      }
+      s.blocks.push_back(b);
+      parent = b;
+    }
+    a->seqs.emplace(seq_id, std::move(s));
+  } catch (...) {
+    return PKV_E_NOMEM;
+  }
+  *cached_tokens_out = shared * bs;
   return PKV_OK;
 }
 

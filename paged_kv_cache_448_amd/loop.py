@@ -4,8 +4,10 @@ Each step of a plan (requests admitted, sequences decoding, sequences leaving;
 see workloads.loop for the plans used in tests and benchmarks):
 
 1. the admitted requests take the blocks of their prompts from the host
-   allocator, and their prompt K/V is written into each layer's pool (one
-   kv_append per layer for all of them, one slot per prompt token);
+   allocator -- sharing the full blocks of a prompt prefix that a live
+   sequence already holds when the prompts come as token ids -- and the K/V of
+   the prompt positions not already cached is written into each layer's pool
+   (one kv_append per layer for all of them, one slot per token);
 2. every running sequence takes the slot of its next token (append_slots: a
    fresh block whenever the last one is full), and the running batch's block
    tables, context lengths and slots are copied to the device;
@@ -94,22 +96,35 @@ class DecodeLoop:
             raise PkvError(f"{name} must be a contiguous {self.dtype} GPU tensor of shape {shape}, got "
                            f"{t.dtype} {tuple(t.shape)}")
 
-    def admit(self, rids, prompt_lens, prompt_kv):
-        """Register requests rids with their prompt lengths and write their prompts' K/V.
+    def admit(self, rids, prompt_lens, prompt_kv, token_ids=None):
+        """Register requests rids with their prompts and write the prompts' K/V.
 
-        prompt_kv(layer) -> (k, v): device tensors [sum(prompt_lens), Hkv, D], the
-        prompts one after the other in the order of rids."""
+        Without token_ids every prompt gets fresh blocks.  With token_ids (one int
+        array per request) the allocator shares the leading full blocks that a live
+        sequence already holds for the same tokens (prefix caching), and only the
+        positions after them are written.  prompt_kv(layer, cached) -> (k, v): device
+        tensors [T, Hkv, D] holding, request after request in the order of rids,
+        positions cached[i] .. prompt_lens[i]-1 (T = the sum of those counts).
+        Returns cached, the per-request count of prompt tokens already in the pool."""
         lc, bs = self.lc, self.lc.block_size
-        slots = []
-        for rid, P in zip(rids, prompt_lens):
-            self.alloc.add_seq(int(rid), int(P))
-            if P:
-                table, _ = self.alloc.block_tables([int(rid)], -(-int(P) // bs))
-                pos = np.arange(int(P), dtype=np.int64)
+        cached, slots = [], []
+        for i, (rid, P) in enumerate(zip(rids, prompt_lens)):
+            P = int(P)
+            if token_ids is None:
+                self.alloc.add_seq(int(rid), P)
+                c = 0
+            else:
+                if len(token_ids[i]) != P:
+                    raise PkvError(f"request {rid}: {len(token_ids[i])} token ids for a {P}-token prompt")
+                c = self.alloc.add_seq_prefix(int(rid), token_ids[i])
+            cached.append(c)
+            if P > c:
+                table, _ = self.alloc.block_tables([int(rid)], -(-P // bs))
+                pos = np.arange(c, P, dtype=np.int64)
                 slots.append(table[0, pos // bs].astype(np.int64) * bs + pos % bs)
         T = int(sum(len(s) for s in slots))
         if T == 0:
-            return
+            return cached
         if T > self.max_prompt_tokens:
             raise PkvError(f"{T} prompt tokens in one step; the loop stages at most {self.max_prompt_tokens}")
         stream = torch.cuda.current_stream(self.device)
@@ -120,12 +135,13 @@ class DecodeLoop:
         shape = (T, lc.num_kv_heads, lc.head_dim)
         sp = ctypes.c_void_p(stream.cuda_stream)
         for layer in range(lc.num_layers):
-            k, v = prompt_kv(layer)
+            k, v = prompt_kv(layer, cached)
             self._check(k, shape, "prompt k")
             self._check(v, shape, "prompt v")
             check(self._lib.pkv_kv_append(_p(k), _p(v), _p(self.prompt_slots_d), T, _p(self.k_pools[layer]),
                                           _p(self.v_pools[layer]), lc.num_blocks, bs, lc.num_kv_heads, lc.head_dim,
                                           self.code, sp))
+        return cached
 
     def decode_step(self, run_ids, step_qkv, outs):
         """One token for every sequence in run_ids (batch order).

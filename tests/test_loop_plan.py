@@ -155,3 +155,17 @@ def test_replay_pins_catch_planted_mistakes(bad):
     ref = oracle_attn.decode(q, kc.ravel(), vc.ravel(), table[None], np.array([L]), CFG.scale, dtype=CFG.dtype,
                              num_blocks=len(table), num_kv_heads=Hkv, block_size=bs)
     assert not np.allclose(got, ref, rtol=0, atol=1e-6)
+
+
+def test_token_values_depend_only_on_the_prefix():
+    lc = wl_loop.LOOP_CONFIGS["tiny-prefix-loop"]
+    a = wl_loop.prompt_tokens(lc, 3, 0, 60)
+    b = wl_loop.prompt_tokens(lc, 3, 3, 60)       # same group (3 groups): same 40-token prefix
+    c = wl_loop.prompt_tokens(lc, 3, 1, 60)       # another group
+    assert np.array_equal(a[:40], b[:40]) and not np.array_equal(a[:40], c[:40])
+    ka, va = wl_loop.token_values(lc, 3, a, 1)
+    kb, vb = wl_loop.token_values(lc, 3, b, 1)
+    first = int(np.argmax(a != b))
+    assert first >= 40
+    assert np.array_equal(ka[:first], kb[:first]) and np.array_equal(va[:first], vb[:first])
+    assert not np.array_equal(ka[first], kb[first])

@@ -51,6 +51,8 @@ class LoopConfig:
     prompt_mean: float = 0.0
     gen_mean: float = 0.0
     arrivals_per_step: float = 0.0  # 0: every request is waiting at step 0
+    prefix_groups: int = 0          # > 0: request r's prompt starts with group (r mod groups)'s
+    prefix_tokens: int = 0          #      prefix of this many tokens (prompts are given as token ids)
 
     @property
     def group(self) -> int:
@@ -69,6 +71,11 @@ LOOP_CONFIGS = {
     # small enough that the fp64 oracle replays every step in seconds
     "tiny-loop": LoopConfig("tiny-loop", 2, 8, 2, 64, 16, BF16, num_blocks=48, max_batch=6, num_requests=14,
                             prompt_lo=1, prompt_hi=70, gen_lo=1, gen_hi=24, arrivals_per_step=0.8),
+    # the same loop with prompts made of token ids, requests in 3 groups sharing a 40-token
+    # prefix (two full blocks and a partial one), for prefix caching
+    "tiny-prefix-loop": LoopConfig("tiny-prefix-loop", 2, 8, 2, 64, 16, BF16, num_blocks=48, max_batch=6,
+                                   num_requests=14, prompt_lo=1, prompt_hi=70, gen_lo=1, gen_hi=24,
+                                   arrivals_per_step=0.8, prefix_groups=3, prefix_tokens=40),
     # Llama-3.2-1B attention shape (16 layers, 32 q / 8 kv heads, head_dim 64, bs 16, bf16) with the
     # length mix of the 256-sequence continuous-batching workload (lognormal, mean 600); a backlog of
     # requests keeps the batch full
@@ -150,6 +157,32 @@ def plan(lc: LoopConfig, seed: int, num_steps: int) -> Tuple[List[Request], List
             reserved -= blocks_for(reqs[rid].prompt_len + reqs[rid].gen_len, lc.block_size)
         steps.append(Step(s, admitted, run, finish))
     return reqs, steps
+
+
+def prompt_tokens(lc: LoopConfig, seed: int, rid: int, prompt_len: int) -> np.ndarray:
+    """Token ids of request rid's prompt (int32 [P]): its group's prefix, then its own tokens."""
+    own = np.random.default_rng([seed, 3, rid]).integers(0, 32000, size=prompt_len).astype(np.int32)
+    if lc.prefix_groups <= 0:
+        return own
+    pre = np.random.default_rng([seed, 4, rid % lc.prefix_groups]).integers(0, 32000, size=lc.prefix_tokens)
+    n = min(prompt_len, lc.prefix_tokens)
+    own[:n] = pre[:n]
+    return own
+
+
+def token_values(lc: LoopConfig, seed: int, tokens, layer: int):
+    """K and V bits [P, Hkv, D] of a prompt given as token ids, where row t depends only on
+    tokens[0..t] (as a model's keys and values do), so equal prefixes give equal rows."""
+    P = len(tokens)
+    k = np.empty((P, lc.num_kv_heads, lc.head_dim), dtype=np.uint16)
+    v = np.empty_like(k)
+    h = 0
+    for t in range(P):
+        h = (h * 1000003 + int(tokens[t]) + 1) % (1 << 61)
+        rng = np.random.default_rng([seed, 5, layer, h])
+        k[t] = random_bits(rng, (lc.num_kv_heads, lc.head_dim), lc.dtype)
+        v[t] = random_bits(rng, (lc.num_kv_heads, lc.head_dim), lc.dtype)
+    return k, v
 
 
 def prompt_values(lc: LoopConfig, seed: int, rid: int, layer: int, prompt_len: int):
