@@ -67,9 +67,19 @@ def encode_value(x: float) -> int:
 
 
 def encode(x) -> np.ndarray:
-    """Elementwise encode_value over an array (uint8 codes)."""
-    flat = np.asarray(x, dtype=np.float64).ravel()
-    return np.array([encode_value(v) for v in flat], dtype=np.uint8).reshape(np.shape(x))
+    """encode_value over an array (uint8 codes): the same nearest-code search, ties to the
+    even code, saturation and NaN rule, taken for all elements at once."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = DECODE_TABLE[:0x7F]                       # finite non-negative codes, increasing
+    a = np.abs(x)
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    c = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where((lo & 1) == 0, lo, hi)))
+    c = np.where(mags[hi] == a, hi, c)               # exactly representable
+    c = np.where(a >= MAX_E4M3, 0x7E, c)             # saturate (infinities too)
+    code = np.where(np.signbit(x), 0x80, 0) | c
+    return np.where(np.isnan(x), NAN_CODE, code).astype(np.uint8)
 
 
 def quantize_for_append(x_f32: np.ndarray, scale: float) -> np.ndarray:

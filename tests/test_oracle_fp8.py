@@ -114,3 +114,19 @@ def test_append_scatters_codes_and_leaves_the_rest():
         for off in range(bs):
             if (n, off) not in touched:
                 assert np.all(kp[n, :, off] == 0x55) and np.all(vp[n, :, off] == 0x55)
+
+
+def test_array_encode_matches_the_scalar_definition():
+    """encode (all elements at once) against encode_value one by one: every code's value,
+    every midpoint between neighbouring codes and a little either side of it, random
+    values over the whole range, and the special values."""
+    finite = fp8.DECODE_TABLE[:0x7F]
+    mids = (finite[1:] + finite[:-1]) / 2
+    rng = np.random.default_rng(3)
+    xs = np.concatenate([finite, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                         rng.standard_normal(3000) * 50, rng.standard_normal(1000) * 1e-3,
+                         [448.0, 464.0, 479.9, 480.0, 1e30, math.inf, -math.inf, math.nan, -math.nan, 0.0, -0.0]])
+    xs = np.concatenate([xs, -xs])
+    want = np.array([fp8.encode_value(float(v)) for v in xs], dtype=np.uint8)
+    got = fp8.encode(xs.reshape(2, -1)).ravel()
+    assert np.array_equal(got, want), xs[got != want][:8]
