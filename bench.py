@@ -59,7 +59,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s (decimal)
 CSRC = os.path.join(ROOT, "paged_kv_cache_448_amd", "csrc")
 # sources whose change invalidates measured counters of the decode kernels
 DECODE_SOURCES = ["common.h", "kernels.h", "decode_common.h", "decode_mfma_kernel.h", "decode_mfma.hip",
-                  "decode_simt.hip", "merge.hip", "api.cpp"]
+                  "decode_fp8.hip", "decode_simt.hip", "merge.hip", "api.cpp"]
 COPY_CALIBRATION_BYTES = 1 << 29  # 512 MiB read and written by the calibration copy
 
 
@@ -143,7 +143,8 @@ def _read_counter_csv(path, counter):
     return rows
 
 
-def pmc_summary(fetch_csv, write_csv, workload_name, decode_bytes, steps_note):
+def pmc_summary(fetch_csv, write_csv, workload_name, decode_bytes, steps_note,
+                kernels=("decode_mfma_kernel", "decode_simt_kernel")):
     """Traffic per decode launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by what the same counter reads for the calibration copy."""
     out = {}
@@ -151,7 +152,7 @@ def pmc_summary(fetch_csv, write_csv, workload_name, decode_bytes, steps_note):
         rows = _read_counter_csv(path, counter)
         # the timed launches: with the fused append the grid carries extra append
         # workgroups, which tells them from the decode-only context loop
-        dec_rows = [(g, v) for n, g, v in rows if "decode_mfma_kernel" in n or "decode_simt_kernel" in n]
+        dec_rows = [(g, v) for n, g, v in rows if any(k in n for k in kernels)]
         top = max((g for g, _ in dec_rows), default=0)
         dec = [v for g, v in dec_rows if g == top]
         mrg = [v for n, g, v in rows if "merge_kernel" in n]
@@ -265,6 +266,160 @@ def loop_bench(name, steps, warmup, seed=11):
     print(json.dumps(rec), flush=True)
 
 
+def fp8_decode_bytes(wl):
+    """Algorithmic bytes of one decode launch over FP8 pools: the unique context
+    K/V at one byte per element, plus q, out, table entries and lengths."""
+    c = wl.cfg
+    B, bs = len(wl.context_lens), c.block_size
+    _, unique16 = algorithmic_bytes(c, wl.context_lens, wl.block_tables, bs)
+    small = 2 * B * c.num_q_heads * c.head_dim * c.elem_bytes + 4 * int(((wl.context_lens + bs - 1) // bs).sum()) + 4 * B
+    return (unique16 - small) // c.elem_bytes + small
+
+
+def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale=0.0125, v_scale=0.01):
+    """Decode step over FP8 (E4M3) pools (see --kv fp8): per layer, kv_append_fp8 of
+    this step's token per sequence, then paged_attn_decode_fp8."""
+    import torch
+
+    import paged_kv_cache_448_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.build(config, poison=False)
+    c = wl.cfg
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[c.dtype]
+    N, Hkv, bs, D = wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim
+    B = len(wl.context_lens)
+
+    def up(a, shape=None):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt)
+        return (t.reshape(shape) if shape else t).to(dev)
+
+    all_slots = torch.arange(N * bs, dtype=torch.int64, device=dev)
+
+    def fp8_pools(k_bits, v_bits):
+        # every slot of the 16-bit pools, quantised by the library's own append
+        def rows(bits):
+            return up(bits, (N, Hkv, bs, D)).permute(0, 2, 1, 3).reshape(N * bs, Hkv, D).contiguous()
+        kp, vp = pkv.new_cache_fp8(N, Hkv, bs, D, dev), pkv.new_cache_fp8(N, Hkv, bs, D, dev)
+        pkv.kv_append_fp8(rows(k_bits), rows(v_bits), all_slots, kp, vp, k_scale, v_scale)
+        return kp, vp
+
+    pool_bytes = 2 * N * Hkv * bs * D * c.num_layers
+    R = 1 if c.num_layers > 1 else max(1, math.ceil((1 << 30) / pool_bytes))
+    layers = []
+    for r in range(R):
+        rl = []
+        for ly in wl.layers:
+            kp, vp = fp8_pools(ly.k_cache, ly.v_cache)
+            rl.append(dict(q=up(ly.q), kc=kp, vc=vp, kn=up(ly.k_new), vn=up(ly.v_new),
+                           out=torch.empty((B, c.num_q_heads, D), dtype=tdt, device=dev)))
+        layers.append(rl)
+    torch.cuda.synchronize()
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens = torch.from_numpy(wl.context_lens).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    mcl = int(wl.context_lens.max())
+    ws = torch.empty(max(pkv.decode_workspace_bytes(B, c.num_q_heads, Hkv, D, bs, mcl), 256), dtype=torch.uint8,
+                     device=dev)
+    part = pkv.plan_partition(B, Hkv, bs, mcl)
+    log(f"fp8 kv: workload {c.name}, rotations R={R} ({R * pool_bytes / 2**30:.2f} GiB of pools), "
+        f"partition plan {part or 'single pass'}")
+
+    def decode(t):
+        pkv.paged_attn_decode_fp8(t["q"], t["kc"], t["vc"], tables, lens, c.scale, k_scale, v_scale, t["out"],
+                                  max_context_len=mcl, workspace=ws)
+
+    def step(i):
+        for t in layers[i % R]:
+            pkv.kv_append_fp8(t["kn"], t["vn"], slots, t["kc"], t["vc"], k_scale, v_scale)
+            decode(t)
+
+    stream = torch.cuda.current_stream(dev)
+    h0 = time.perf_counter()
+    for i in range(warmup):
+        step(i)
+    host_per_step = (time.perf_counter() - h0) / max(warmup, 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_us = (1 << 20) / max(1e3 * e0.elapsed_time(e1), 1e-3)
+    head_us = max(2000.0, 1.5e6 * host_per_step * steps)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(head_us * cycles_per_us))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    ms_step = timed(step) / steps
+    dec_us = 1e3 * timed(lambda i: [decode(t) for t in layers[i % R]]) / (steps * c.num_layers)
+
+    if copy_calibration:
+        src = torch.empty(COPY_CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    unique = fp8_decode_bytes(wl)
+    app = 2 * B * Hkv * D * (c.elem_bytes + 1) + 8 * B
+    value = c.num_layers * (unique + app) / (ms_step * 1e-3) / 1e9
+    dec_gbs = unique / (dec_us * 1e-6) / 1e9
+    log(f"fp8 step {ms_step * 1e3:.1f} us; decode call {dec_us:.2f} us over {unique / 1e6:.2f} MB -> {dec_gbs:.0f} GB/s "
+        f"= {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak")
+    cpu = None
+    if cpu_budget > 0:
+        from oracle import fp8 as ofp8
+        ly = wl.layers[0]
+        # the oracle's append of the contexts is the sample's setup, not timed
+        rows = lambda bits: bits.reshape(N, Hkv, bs, D).transpose(0, 2, 1, 3).reshape(N * bs, Hkv, D)  # noqa: E731
+        kc = np.full((N, Hkv, bs, D), ofp8.NAN_CODE, np.uint8)
+        vc = np.full_like(kc, ofp8.NAN_CODE)
+        ctx = np.unique(np.concatenate([wl.block_tables[i, np.arange(int(L)) // bs].astype(np.int64) * bs
+                                        + np.arange(int(L)) % bs for i, L in enumerate(wl.context_lens)]))
+        ofp8.append(rows(ly.k_cache)[ctx], rows(ly.v_cache)[ctx], c.dtype, ctx, kc, vc, k_scale, v_scale,
+                    num_blocks=N, block_size=bs)
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            ofp8.decode(ly.q, kc, vc, k_scale, v_scale, wl.block_tables, wl.context_lens, c.scale, q_dtype=c.dtype,
+                        num_blocks=N, num_kv_heads=Hkv, block_size=bs)
+            runs += 1
+            if time.perf_counter() - t0 >= cpu_budget:
+                break
+        dt = (time.perf_counter() - t0) / runs
+        cpu = {"value": round(unique / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle.fp8.decode over the whole first layer ({B} sequences), {runs} passes, "
+                         f"{dt:.3f} s per pass", "tokens_per_s": round(B / dt, 2)}
+    traffic = load_traffic(c.name + "-fp8")
+    if traffic is not None:
+        traffic = int(round(traffic))
+    rec = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+           "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": f"kv fp8-e4m3, q/out/mfma {c.dtype}", "data": "synthetic",
+           "config": {"workload": f"{c.name} over FP8 (E4M3) pools: kv_append_fp8 + paged_attn_decode_fp8 of {B} "
+                                  f"sequences, {c.num_layers} layer(s), {c.num_q_heads}q/{Hkv}kv heads, head_dim {D}, "
+                                  f"block_size {bs}", "config_id": config, "kv": "fp8_e4m3",
+                      "k_scale": k_scale, "v_scale": v_scale, "partition_tokens": part, "rotations": R},
+           "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1), "decode_call_us": round(dec_us, 2),
+           "decode_bytes_unique": unique,
+           "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "kernel": "decode_fp8_kernel (paged_attn_decode_fp8 call)"},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +436,8 @@ def main():
                     help="capture the K timed steps into one HIP graph and replay it (fused path only)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--loop", default=None, help="continuous-batching loop workload (e.g. cb-llama3.2-1b)")
+    ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
+                    help="fp8: the step over FP8 (E4M3) pools (kv_append_fp8 + paged_attn_decode_fp8)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -291,10 +448,18 @@ def main():
     if args.loop:
         loop_bench(args.loop, args.steps, args.warmup)
         return
+    if args.kv == "fp8" and not args.pmc_summary:
+        fp8_bench(args.config, args.steps, args.warmup, args.cpu_budget, args.copy_calibration)
+        return
 
     import workloads
     if args.pmc_summary:
         wl = workloads.build(args.config, poison=False)
+        if args.kv == "fp8":
+            pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name + "-fp8", fp8_decode_bytes(wl),
+                        f"bench.py --kv fp8 --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+                        f"--cpu-budget 0 --copy-calibration", kernels=("decode_fp8_kernel",))
+            return
         _, unique = algorithmic_bytes(wl.cfg, wl.context_lens, wl.block_tables, wl.cfg.block_size)
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name, unique,
                     f"bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "

@@ -202,6 +202,66 @@ int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_
  */
 int pkv_decode_supported(int32_t impl, int32_t dtype, int32_t head_dim, int32_t group);
 
+/*
+ * FP8 KV cache.  The Tiny-vLLM summary ("[Hacker News 요약] C++와 CUDA로 vLLM의
+ * 경량 고성능 LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section "향후 전망") names
+ * an FP8 datatype as a next step and fixes nothing more; this library takes
+ * the E4M3 format (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+ * subnormals, no infinities, S.1111.111 = NaN, largest finite 448) with one
+ * fp32 scale per pool: a stored code c stands for e4m3(c) * scale.  The pools
+ * have the 16-bit layout above with one byte per element:
+ *
+ *   k_cache, v_cache: uint8 [N][Hkv][bs][D], code of (n,h,t,d) at byte
+ *            ((n*Hkv + h)*bs + t)*D + d
+ *
+ * Decode reads half the bytes of a 16-bit cache, and decode time is the time
+ * to read the cache ("vLLM -- PagedAttention으로 LLM 추론 성능을 2~4배 끌어올린
+ * 서빙 엔진", section "Prefill vs Decode").
+ */
+
+/*
+ * pkv_kv_append_fp8 -- pkv_kv_append into FP8 pools.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] in src_dtype (PKV_BF16 or
+ *                 PKV_FP16).
+ *   k_scale, v_scale  the pools' scales, positive and finite.
+ * Each element x is stored as the code nearest to fp32(x * fp32(1 / scale))
+ * (ties to the even code), with magnitudes above 448 (infinities included)
+ * saturating to +-448 (0x7E / 0xFE) and NaN stored as 0x7F.  Slots as in
+ * pkv_kv_append (negative or >= num_blocks*block_size: nothing written;
+ * distinct otherwise).  Only the bytes of the written slots change.
+ * Supported: as pkv_kv_append.  Errors: PKV_E_NULL, PKV_E_SHAPE (also a scale
+ * that is not positive and finite), PKV_E_UNSUPPORTED, PKV_E_HIP.
+ */
+int pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                      void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t src_dtype, float k_scale, float v_scale, hipStream_t stream);
+
+/*
+ * pkv_paged_attn_decode_fp8 -- pkv_paged_attn_decode_ex over FP8 pools:
+ * out = softmax(scale * q K^T) V with K = e4m3(k_cache) * k_scale and
+ * V = e4m3(v_cache) * v_scale.
+ *
+ *   q, out        [num_seqs][num_q_heads][head_dim] in dtype (PKV_BF16 / PKV_FP16).
+ *   k_scale, v_scale  positive and finite.
+ *   the other arguments are those of pkv_paged_attn_decode_ex; the workspace is
+ *   sized by the same pkv_decode_workspace_bytes_ex query.
+ * Every code is exact in dtype, so the kernel runs the 16-bit MFMA tiles on
+ * the widened codes; k_scale is folded into the softmax scale and v_scale
+ * into the output (not into any element).  Tails, empty and invalid
+ * sequences as in pkv_paged_attn_decode.  A NaN code inside a context makes
+ * the heads that read it NaN.
+ * Supported: as the MFMA kernel (pkv_decode_supported(PKV_IMPL_MFMA, ...)).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE, PKV_E_UNSUPPORTED, PKV_E_WORKSPACE, PKV_E_HIP.
+ */
+int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t max_context_len, float scale, float k_scale,
+                              float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,9 @@ Names mirror the C ABI in include/pkv.h and include/pkv_alloc.h:
 * ``paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
 * ``append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
   context_lens, scale, out)`` -- both in one launch (one decode step of one layer)
+* ``kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)`` and
+  ``paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, out)``
+  -- the same over FP8 (E4M3) pools (uint8 tensors, see ``new_cache_fp8``)
 * ``BlockAllocator`` -- the host-side block allocator.
 
 Caches are tensors of shape ``(num_blocks, num_kv_heads, block_size, head_dim)``
@@ -24,8 +27,9 @@ import torch
 
 from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
 
-__all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes", "decode_supported", "plan_partition", "new_cache",
-           "cache_dims", "BlockAllocator", "PkvError", "lib"]
+__all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes",
+           "decode_supported", "plan_partition", "new_cache", "new_cache_fp8", "cache_dims", "kv_append_fp8",
+           "paged_attn_decode_fp8", "BlockAllocator", "PkvError", "lib"]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
 IMPLS = {"auto": 0, "simt": 1, "mfma": 2}
@@ -65,6 +69,11 @@ def new_cache(num_blocks, num_kv_heads, block_size, head_dim, dtype=torch.bfloat
     """Uninitialised K or V pool in the library's layout."""
     _need(block_size % 16 == 0, "block_size must be a multiple of 16")
     return torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+
+
+def new_cache_fp8(num_blocks, num_kv_heads, block_size, head_dim, device="cuda"):
+    """Uninitialised FP8 (E4M3 code per element) K or V pool in the library's layout."""
+    return new_cache(num_blocks, num_kv_heads, block_size, head_dim, torch.uint8, device)
 
 
 def cache_dims(cache):
@@ -189,6 +198,71 @@ def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
         _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
         _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
+    return out
+
+
+def _scale(x, name):
+    x = float(x)
+    _need(x > 0 and x < float("inf"), f"{name} must be positive and finite, got {x}")
+    return ctypes.c_float(x)
+
+
+def kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale):
+    """Quantise k/v ([T, Hkv, D], bf16 or fp16) to E4M3 codes of x / scale and write them
+    into the slots ``slot_mapping`` (int64 [T]) of the uint8 pools."""
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _device_tensor(t, name, torch.uint8)
+    _device_tensor(k, "k", None, 3)
+    code = _dtype_code(k)
+    for name, t in (("k", k), ("v", v)):
+        _device_tensor(t, name, k.dtype, 3)
+        _need(tuple(t.shape[1:]) == (Hkv, D), f"{name} must be [T, {Hkv}, {D}], got {tuple(t.shape)}")
+    _need(k.shape == v.shape, "k and v differ in shape")
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+    _need(slot_mapping.shape[0] == k.shape[0], "slot_mapping must have one slot per token")
+    check(lib().pkv_kv_append_fp8(_ptr(k), _ptr(v), _ptr(slot_mapping), k.shape[0], _ptr(k_cache), _ptr(v_cache),
+                                  N, bs, Hkv, D, code, _scale(k_scale, "k_scale"), _scale(v_scale, "v_scale"),
+                                  _stream(k_cache)))
+
+
+def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, out=None, *,
+                          max_context_len=None, workspace=None, partition_tokens=0):
+    """paged_attn_decode over FP8 pools: K = e4m3(k_cache) * k_scale, V = e4m3(v_cache) * v_scale.
+
+    q (bf16 or fp16) [B, Hq, D]; the pools are uint8 tensors from new_cache_fp8;
+    the other arguments as paged_attn_decode.  Returns ``out`` ([B, Hq, D], q's dtype).
+    """
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(k_cache, "k_cache", torch.uint8)
+    _device_tensor(v_cache, "v_cache", torch.uint8)
+    _device_tensor(q, "q", None, 3)
+    code = _dtype_code(q)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    check(lib().pkv_paged_attn_decode_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
+        ctypes.c_float(scale), _scale(k_scale, "k_scale"), _scale(v_scale, "v_scale"), _ptr(out), B, Hq, Hkv, D, bs,
+        N, code, _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
     return out
 
 

@@ -146,11 +146,19 @@ struct FusedAppend {
   const int64_t* slot_mapping;
 };
 
+// Scales of FP8 (E4M3) pools (nullptr: 16-bit pools).
+struct Fp8Scales {
+  float k, v;
+};
+
+bool scale_ok(float s) { return s > 0.f && s <= 3.4e38f; }  // positive and finite (NaN fails both)
+
 int decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len, float scale,
                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace, size_t workspace_bytes,
-                int32_t partition_tokens, int32_t impl, const FusedAppend& app, hipStream_t stream) {
+                int32_t partition_tokens, int32_t impl, const FusedAppend& app, const Fp8Scales* fp8,
+                hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_E_SHAPE;
@@ -182,6 +190,8 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
     default: return PKV_E_UNSUPPORTED;
   }
   if (fused && !use_mfma) return PKV_E_UNSUPPORTED;  // the append is fused into the MFMA kernel only
+  if (fp8 && (fused || !use_mfma)) return PKV_E_UNSUPPORTED;  // FP8 pools: MFMA kernel, no fused append
+  if (fp8 && (!scale_ok(fp8->k) || !scale_ok(fp8->v))) return PKV_E_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
   if (fused && (!app.k_new || !app.v_new)) return PKV_E_NULL;
@@ -228,9 +238,12 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.max_context_len = max_context_len;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
-  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? fp8->k : 1.0) * kLog2e);
+  p.out_scale = fp8 ? fp8->v : 1.f;
 
-  hipError_t e = use_mfma ? pkv::launch_decode_mfma(p, dtype, stream) : pkv::launch_decode_simt(p, dtype, stream);
+  hipError_t e = fp8        ? pkv::launch_decode_fp8(p, dtype, stream)
+                 : use_mfma ? pkv::launch_decode_mfma(p, dtype, stream)
+                            : pkv::launch_decode_simt(p, dtype, stream);
   if (e != hipSuccess) return PKV_E_HIP;
   if (plan.num_parts > 1) {
     e = pkv::launch_merge(p, dtype, stream);
@@ -250,7 +263,7 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
                              int32_t impl, hipStream_t stream) {
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
-                     workspace_bytes, partition_tokens, impl, FusedAppend{nullptr, nullptr, nullptr}, stream);
+                     workspace_bytes, partition_tokens, impl, FusedAppend{nullptr, nullptr, nullptr}, nullptr, stream);
 }
 
 int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v_new,
@@ -264,7 +277,7 @@ int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping},
-                     stream);
+                     nullptr, stream);
 }
 
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -277,6 +290,49 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                                   max_context_len, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   block_size, num_blocks, dtype, workspace, workspace_bytes, 0, PKV_IMPL_AUTO,
                                   stream);
+}
+
+int pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                      void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t src_dtype, float k_scale, float v_scale, hipStream_t stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PKV_E_SHAPE;
+  if (!dtype_ok(src_dtype) || !block_size_ok(block_size) || head_dim <= 0 || head_dim % 8 || head_dim > 512)
+    return PKV_E_UNSUPPORTED;
+  if (!scale_ok(k_scale) || !scale_ok(v_scale)) return PKV_E_SHAPE;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return PKV_E_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PKV_E_SHAPE;
+  if (static_cast<int64_t>(num_tokens) * num_kv_heads * (head_dim / 8) > static_cast<int64_t>(INT_MAX) * 256)
+    return PKV_E_SHAPE;
+  pkv::AppendFp8Params p;
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.slot_mapping = slot_mapping;
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.k_inv_scale = 1.f / k_scale;
+  p.v_inv_scale = 1.f / v_scale;
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.block_size = block_size;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.src_fp16 = src_dtype == PKV_FP16;
+  return pkv::launch_kv_append_fp8(p, stream) == hipSuccess ? PKV_OK : PKV_E_HIP;
+}
+
+int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t max_context_len, float scale, float k_scale,
+                              float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                              hipStream_t stream) {
+  const Fp8Scales sc{k_scale, v_scale};
+  return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
+                     workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{nullptr, nullptr, nullptr}, &sc,
+                     stream);
 }
 
 }  // extern "C"

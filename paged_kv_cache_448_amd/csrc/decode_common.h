@@ -50,8 +50,10 @@ __device__ __forceinline__ void write_degenerate(const DecodeParams& p, const Wo
 }
 
 // Fold NW waves' states (in LDS) and store either the final output (the whole
-// context was one partition) or this partition's partial state.
-template <typename T, int D, int G, int NW>
+// context was one partition) or this partition's partial state.  kScaleOut:
+// the accumulator is multiplied by p.out_scale first (partials carry it, so
+// the merge needs nothing).
+template <typename T, int D, int G, int NW, bool kScaleOut = false>
 __device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const float (*sm_l)[G],
                                                   const float (*sm_o)[G][D], const DecodeParams& p,
                                                   const WorkItem& w, bool single) {
@@ -67,6 +69,7 @@ __device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const 
       lt = fmaf(c, sm_l[k][h], lt);
       o = fmaf(c, sm_o[k][h][d], o);
     }
+    if (kScaleOut) o *= p.out_scale;
     const size_t row = static_cast<size_t>(w.seq) * p.num_q_heads + w.kvh * G + h;
     if (single) {
       p.out[row * D + d] = to_bits<T>(o / lt);

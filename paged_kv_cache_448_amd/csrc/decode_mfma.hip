@@ -7,10 +7,10 @@ namespace {
 
 // Sub-tiles each wave keeps in flight, and the waves per SIMD the register
 // allocation must leave room for (measured on the Llama-3.2-1B batch and the
-// LLaMA-2-70B layer): four sub-tiles (16 KB) at head_dim 64 with the
-// compiler's own allocation (three waves per SIMD; forcing four costs more in
-// scheduling than it gains), two sub-tiles (16 KB) at head_dim 128 at three
-// waves per SIMD, the most that does not spill.
+// LLaMA-2-70B layer): four sub-tiles (16 KB) at head_dim 64, two sub-tiles
+// (16 KB) at head_dim 128; both at three waves per SIMD (the kernel caps it
+// there: four measured slower at head_dim 64; at head_dim 128 three is the
+// most that does not spill).
 template <int D> struct MfmaShape;
 template <> struct MfmaShape<64> { static constexpr int kDepth = 4, kMinWaves = 2; };
 template <> struct MfmaShape<128> { static constexpr int kDepth = 2, kMinWaves = 3; };

@@ -75,6 +75,10 @@ template <> struct Mma<Bf16> {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, x2));
   }
+  // a + lo(w) + hi(w) for a word of two bf16 values (one dot2 instruction)
+  static __device__ __forceinline__ float sum2(uint32_t w, float a) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(x2, w), __builtin_bit_cast(x2, 0x3f803f80u), a, false);
+  }
 };
 
 template <> struct Mma<Fp16> {
@@ -90,6 +94,9 @@ template <> struct Mma<Fp16> {
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, x2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t w, float a) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(x2, w), __builtin_bit_cast(x2, 0x3c003c00u), a, false);
   }
 };
 
@@ -124,9 +131,9 @@ template <int D> struct Tile {
 template <int D>
 __device__ __forceinline__ u32x2 v_operand(const VSlice<D> (&v)[4], int j) {
   const int w = j >> 1;
-  if ((j & 1) == 0)
-    return u32x2{(v[0].w[w] & 0xffffu) | (v[1].w[w] << 16), (v[2].w[w] & 0xffffu) | (v[3].w[w] << 16)};
-  return u32x2{(v[0].w[w] >> 16) | (v[1].w[w] & 0xffff0000u), (v[2].w[w] >> 16) | (v[3].w[w] & 0xffff0000u)};
+  // byte permute: the low (j even) or high (j odd) 16-bit halves of two words
+  const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+  return u32x2{__builtin_amdgcn_perm(v[1].w[w], v[0].w[w], sel), __builtin_amdgcn_perm(v[3].w[w], v[2].w[w], sel)};
 }
 
 // Fused append, store side: the same bytes kv_append writes for token i =
@@ -160,15 +167,19 @@ __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
   }
 }
 
-// MINW: waves per SIMD the register allocation must allow (launch-bound
-// minimum); the launcher picks S and MINW per head size so that nothing spills.
+// MINW: waves per SIMD the register allocation must allow; the launcher picks
+// S and MINW per head size so that nothing spills.  At most three waves per
+// SIMD: with the head_dim 64 tile the allocation would otherwise fit four,
+// which measured slower on the Llama-3.2-1B batch.
 template <typename T, int D, int G, int NW, int S, int MINW>
-__global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodeParams p) {
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
+decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
   static_assert(NW * kWave >= D, "one thread per dimension stages the appended token");
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
-  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int r = lane & 15, kg = lane >> 4;
   if (static_cast<int>(blockIdx.x) < p.append_wgs) {
     append_tokens<D, NW * kWave>(p);
@@ -330,7 +341,7 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_mfma_kernel(DecodePar
     m = mn;
     const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
     const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
-    l = l * al + ((lo_f32<T>(p01) + hi_f32<T>(p01)) + (lo_f32<T>(p23) + hi_f32<T>(p23)));
+    l = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l * al));
     if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
 #pragma unroll
       for (int j = 0; j < JV; ++j) o[j] *= al;

@@ -16,6 +16,18 @@ struct AppendParams {
   int32_t num_tokens, num_blocks, block_size, num_kv_heads, head_dim;
 };
 
+// FP8 (E4M3) append: 16-bit rows in, one byte per element out, each element
+// rounded to the nearest code of x * inv_scale (saturating, NaN -> 0x7F).
+struct AppendFp8Params {
+  const uint16_t* k;            // [T, Hkv, D], 16-bit (src_fp16 selects fp16, else bf16)
+  const uint16_t* v;
+  const int64_t* slot_mapping;  // [T]
+  uint8_t* k_cache;             // [N, Hkv, bs, D] codes
+  uint8_t* v_cache;
+  float k_inv_scale, v_inv_scale;
+  int32_t num_tokens, num_blocks, block_size, num_kv_heads, head_dim, src_fp16;
+};
+
 struct DecodeParams {
   const uint16_t* q;             // [B, Hq, D]
   const uint16_t* k_cache;
@@ -39,7 +51,8 @@ struct DecodeParams {
   int32_t max_blocks_per_seq, max_context_len;
   int32_t part_tokens;           // tokens per partition, a multiple of 16
   int32_t num_parts;             // ceil(max_context_len / part_tokens), >= 1
-  float scale_log2;              // softmax scale * log2(e)
+  float scale_log2;              // softmax scale * log2(e) (FP8 pools: times the K scale)
+  float out_scale;               // factor on every output (FP8 pools: the V scale; else 1)
 };
 
 // Most tokens one decode workgroup takes (both kernels); longer contexts are
@@ -50,12 +63,16 @@ constexpr int32_t kMaxPartitionTokens = 8192;
 constexpr int32_t kFourWaveMaxTokens = 4096;
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
+hipError_t launch_kv_append_fp8(const AppendFp8Params& p, hipStream_t stream);
 
 bool simt_supported(int dtype, int head_dim, int group);
 hipError_t launch_decode_simt(const DecodeParams& p, int dtype, hipStream_t stream);
 
 bool mfma_supported(int dtype, int head_dim, int group);
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, hipStream_t stream);
+
+// FP8 (E4M3) pools (k_cache / v_cache hold one code per element); no fused append.
+hipError_t launch_decode_fp8(const DecodeParams& p, int dtype, hipStream_t stream);
 
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream);
 

@@ -121,3 +121,43 @@ def _fused(**kw):
 ])
 def test_fused_append_decode_rejects_bad_arguments_before_launch(kw, status):
     assert _fused(**kw) == status
+
+
+def _append_fp8(**kw):
+    a = dict(k=16, v=16, sm=16, T=3, kc=16, vc=16, N=4, bs=16, Hkv=2, D=64, dt=0, ks=0.5, vs=0.25)
+    a.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return pkv.lib().pkv_kv_append_fp8(p(a["k"]), p(a["v"]), p(a["sm"]), a["T"], p(a["kc"]), p(a["vc"]), a["N"],
+                                       a["bs"], a["Hkv"], a["D"], a["dt"], ctypes.c_float(a["ks"]),
+                                       ctypes.c_float(a["vs"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=NULL), E_NULL), (dict(vc=NULL), E_NULL), (dict(T=-1), E_SHAPE), (dict(kc=8), E_SHAPE),
+    (dict(ks=0.0), E_SHAPE), (dict(vs=-1.0), E_SHAPE), (dict(ks=float("inf")), E_SHAPE), (dict(vs=float("nan")), E_SHAPE),
+    (dict(D=12), E_UNSUPPORTED), (dict(bs=8), E_UNSUPPORTED), (dict(dt=2), E_UNSUPPORTED), (dict(T=0, k=NULL), OK),
+])
+def test_append_fp8_rejects_bad_arguments_before_launch(kw, status):
+    assert _append_fp8(**kw) == status
+
+
+def _decode_fp8(**kw):
+    a = dict(q=16, kc=16, vc=16, bt=16, mb=4, cl=16, mcl=64, scale=0.125, ks=0.5, vs=0.25, out=16, B=2, Hq=4, Hkv=2,
+             D=64, bs=16, N=8, dt=0, ws=NULL, wsb=0, pt=0)
+    a.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return pkv.lib().pkv_paged_attn_decode_fp8(
+        p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]), a["mcl"], ctypes.c_float(a["scale"]),
+        ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+        a["N"], a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), E_NULL), (dict(kc=NULL), E_NULL), (dict(out=NULL), E_NULL),
+    (dict(ks=0.0), E_SHAPE), (dict(vs=float("inf")), E_SHAPE), (dict(ks=float("nan")), E_SHAPE),
+    (dict(Hq=6, Hkv=4), E_SHAPE), (dict(mcl=65), E_SHAPE), (dict(pt=24), E_SHAPE), (dict(vc=8), E_SHAPE),
+    (dict(D=96), E_UNSUPPORTED), (dict(dt=4), E_UNSUPPORTED), (dict(Hq=64, Hkv=2), E_UNSUPPORTED),
+    (dict(pt=16), E_WORKSPACE), (dict(B=0), OK),
+])
+def test_decode_fp8_rejects_bad_arguments_before_launch(kw, status):
+    assert _decode_fp8(**kw) == status
