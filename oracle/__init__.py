@@ -29,10 +29,12 @@ order, whether the context length counts the appended token, what a padding
 entry or a tail slot holds) are stated in the module that takes them.
 
 Modules: numerics (bf16/fp16 bits to float64), layout (where an element lives
-inside the physical cache), attention (the decode definition), append (the
-slot scatter), brute (scalar loops for tiny cases), alloc_check (validity of
-block tables and slots), kv_bytes (KV-size accounting).
+inside the physical cache), attention (the decode definition), prefill (causal
+attention of many new tokens per sequence), append (the slot scatter), brute
+(scalar loops for tiny cases), alloc_check (validity of block tables and
+slots), kv_bytes (KV-size accounting), fp8 (the E4M3 KV cache), loop (replay
+of a continuous-batching plan).
 """
-from . import numerics, layout, attention, append, brute, alloc_check, kv_bytes  # noqa: F401
+from . import numerics, layout, attention, append, brute, alloc_check, kv_bytes, prefill  # noqa: F401
 from .attention import decode  # noqa: F401
 from .append import kv_append  # noqa: F401
