@@ -34,6 +34,11 @@ Other modes (measurement tooling):
                       (FETCH_SIZE, then WRITE_SIZE) into the traffic summary
                       under profiles/ that later runs report as
                       roofline.traffic while the decode sources are unchanged.
+  --kv fp8            the step over FP8 (E4M3) pools: kv_append_fp8 + paged
+                      decode over the quantised pools; its own JSON line.
+  --prefill           paged prefill: every context of the workload is a prompt
+                      whose tokens are all new; reports TFLOP/s of the causal
+                      attention against the dense MFMA peak; its own JSON line.
   --loop NAME         continuous-batching loop instead of one batch: requests
                       are admitted (prompt K/V written), decode one token per
                       step over all layers, and leave, for W + K steps of a
@@ -266,6 +271,103 @@ def loop_bench(name, steps, warmup, seed=11):
     print(json.dumps(rec), flush=True)
 
 
+def prefill_flops(lens, new, num_q_heads, head_dim):
+    """Matrix-core flops of causal prefill: each new token at position p scores and
+    accumulates over p + 1 keys, 2*D flops each for q.K and for P.V, per q head."""
+    total = 0
+    for L, n in zip(lens, new):
+        L, n = int(L), int(n)
+        # sum over positions p = L-n .. L-1 of (p + 1)
+        total += n * (2 * L - n + 1) // 2
+    return 4 * head_dim * num_q_heads * total
+
+
+def prefill_bench(config, steps, warmup, cpu_budget):
+    """Paged prefill of whole prompts (see --prefill): every context of the workload is a
+    prompt whose tokens are all new."""
+    import torch
+
+    import paged_kv_cache_448_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.build(config, poison=False)
+    c = wl.cfg
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16}[c.dtype]
+    lens = wl.context_lens
+    new = [int(x) for x in lens]
+    B, T = len(new), int(sum(new))
+    rng = np.random.default_rng(5)
+    q_bits = workloads.random_bits(rng, (T, c.num_q_heads, c.head_dim), c.dtype)
+
+    def up(a, shape=None):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(tdt)
+        return (t.reshape(shape) if shape else t).to(dev)
+
+    shape = (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    ly = wl.layers[0]
+    q = up(q_bits)
+    kc, vc = up(ly.k_cache, shape), up(ly.v_cache, shape)
+    out = torch.empty_like(q)
+    tables = torch.from_numpy(wl.block_tables).to(dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    qs = torch.from_numpy(np.concatenate([[0], np.cumsum(new)]).astype(np.int32)).to(dev)
+    mql, mcl = max(new), int(lens.max())
+
+    def call(i):
+        pkv.paged_prefill(q, kc, vc, tables, lens_d, qs, c.scale, out, max_query_len=mql, max_context_len=mcl)
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(steps):
+        call(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / steps
+    flops = prefill_flops(lens, new, c.num_q_heads, c.head_dim)
+    tfs = flops / (us * 1e-6) / 1e12
+    peak = 2500.0  # MI355X dense bf16 / fp16 MFMA, TFLOP/s
+    log(f"prefill {c.name}: {B} prompts, {T} tokens, {flops / 1e9:.1f} GFLOP per call; {us:.1f} us per call -> "
+        f"{tfs:.1f} TFLOP/s = {100 * tfs / peak:.1f}% of the dense MFMA peak")
+    cpu = None
+    if cpu_budget > 0:
+        from oracle.prefill import prefill as oracle_prefill
+        # sample: the shortest prompts, whole, until the budget is spent
+        order = np.argsort(lens)
+        done_flops, t0, used = 0, time.perf_counter(), []
+        for i in order:
+            sub_qs = np.array([0, new[i]])
+            s0 = int(np.concatenate([[0], np.cumsum(new)])[i])
+            oracle_prefill(q_bits[s0:s0 + new[i]], ly.k_cache, ly.v_cache, wl.block_tables[i:i + 1], lens[i:i + 1],
+                           sub_qs, c.scale, dtype=c.dtype, num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads,
+                           block_size=c.block_size)
+            done_flops += prefill_flops(lens[i:i + 1], new[i:i + 1], c.num_q_heads, c.head_dim)
+            used.append(int(new[i]))
+            if time.perf_counter() - t0 >= cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle.prefill over {len(used)} whole prompts of the batch ({sum(used)} tokens, "
+                         f"the shortest first), {dt:.1f} s"}
+    rec = {"metric": "paged prefill attention TFLOP/s (% of MI355X dense MFMA peak)", "value": round(tfs, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": round(us / 1e3, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c.dtype, "data": "synthetic",
+           "config": {"workload": f"{c.name} contexts as whole prompts: paged_prefill of {B} prompts, {T} tokens, "
+                                  f"{c.num_q_heads}q/{c.num_kv_heads}kv heads, head_dim {c.head_dim}, "
+                                  f"block_size {c.block_size}", "config_id": config, "flops_per_call": flops},
+           "prefill_tokens_per_s": round(T / (us * 1e-6), 1),
+           "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(tfs / peak, 4), "traffic": None, "kernel": "prefill_mfma_kernel"},
+           "cpu_baseline": cpu}
+    print(json.dumps(rec), flush=True)
+
+
 def fp8_decode_bytes(wl):
     """Algorithmic bytes of one decode launch over FP8 pools: the unique context
     K/V at one byte per element, plus q, out, table entries and lengths."""
@@ -436,6 +538,8 @@ def main():
                     help="capture the K timed steps into one HIP graph and replay it (fused path only)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--loop", default=None, help="continuous-batching loop workload (e.g. cb-llama3.2-1b)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="paged prefill of the workload's contexts as whole prompts (TFLOP/s)")
     ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
                     help="fp8: the step over FP8 (E4M3) pools (kv_append_fp8 + paged_attn_decode_fp8)")
     args = ap.parse_args()
@@ -447,6 +551,9 @@ def main():
 
     if args.loop:
         loop_bench(args.loop, args.steps, args.warmup)
+        return
+    if args.prefill:
+        prefill_bench(args.config, args.steps, args.warmup, args.cpu_budget)
         return
     if args.kv == "fp8" and not args.pmc_summary:
         fp8_bench(args.config, args.steps, args.warmup, args.cpu_budget, args.copy_calibration)

@@ -1,12 +1,18 @@
 /*
  * pkv.h -- C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
  *
- * Two device operations and their workspace query:
+ * Device operations:
  *
  *   pkv_kv_append          writes the K/V of new tokens into their cache slots;
  *   pkv_paged_attn_decode  single-token attention of every sequence over its
  *                          cached context, read block by block through a
- *                          per-sequence block table, with GQA head sharing.
+ *                          per-sequence block table, with GQA head sharing
+ *                          (_ex: tuning knobs; pkv_append_paged_attn_decode:
+ *                          both in one launch);
+ *   pkv_paged_prefill      causal attention of many new tokens per sequence
+ *                          over the same paged context;
+ *   pkv_kv_append_fp8, pkv_paged_attn_decode_fp8
+ *                          the append and the decode over FP8 (E4M3) pools.
  *
  * What they compute follows the pages this library was written from:
  * the KV cache is cut into fixed-size blocks, logical blocks of a sequence map
@@ -201,6 +207,48 @@ int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_
  * this dtype, head_dim and GQA group size G = Hq / Hkv, else 0.
  */
 int pkv_decode_supported(int32_t impl, int32_t dtype, int32_t head_dim, int32_t group);
+
+/*
+ * pkv_paged_prefill -- causal attention of many new tokens per sequence over
+ * the paged cache (prompt prefill, or a chunk of one).
+ *
+ * Prefill takes all prompt tokens at once ("vLLM -- PagedAttention으로 LLM
+ * 추론 성능을 2~4배 끌어올린 서빙 엔진", section "Prefill vs Decode"); each token
+ * attends to itself and to earlier positions only ("[Hacker News 요약] C++와
+ * CUDA로 vLLM의 경량 고성능 LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section
+ * "고성능 추론을 위한 고급 최적화 기법", causal mask; same formula and GQA as
+ * decode).
+ *
+ *   q             [num_tokens][num_q_heads][head_dim]: the new tokens of all
+ *                 sequences, packed; sequence i's are rows
+ *                 query_start[i] .. query_start[i+1]-1.
+ *   query_start   [num_seqs + 1] int32, device: non-decreasing, query_start[0] = 0,
+ *                 query_start[num_seqs] = num_tokens.  n_i = query_start[i+1] -
+ *                 query_start[i] may be 0.
+ *   context_lens  [num_seqs] int32, device: L_i >= n_i, the context including the
+ *                 new tokens.  New token j of sequence i is position L_i - n_i + j
+ *                 and attends to positions 0 .. L_i - n_i + j; positions before
+ *                 L_i - n_i are a prefix already in the pool (a cached prompt
+ *                 prefix or an earlier chunk).  The K/V of all L_i positions must
+ *                 be in the pools (pkv_kv_append of the new tokens first).
+ *   max_query_len host bound of every n_i (sizes the grid); max_context_len host
+ *                 bound of every L_i, at most max_blocks_per_seq * block_size.
+ *   out           [num_tokens][num_q_heads][head_dim] in dtype.
+ *   the pools, block_tables and scale as in pkv_paged_attn_decode.
+ *
+ * A sequence with n_i > max_query_len, L_i < n_i or L_i above the bounds gets NaN
+ * in its rows (rows past the first max_query_len are not written); a block id
+ * outside the pool makes the heads that read it NaN.  Inconsistent query_start
+ * entries (negative, decreasing, or past num_tokens): that sequence's rows are
+ * not written.  No workspace.
+ * Supported: as the MFMA decode kernel (head_dim 64 or 128, G in {1, 2, 4, 8, 16}).
+ * Errors: PKV_E_NULL, PKV_E_SHAPE, PKV_E_UNSUPPORTED, PKV_E_HIP.
+ */
+int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
+                      int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale, void* out,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t dtype, hipStream_t stream);
 
 /*
  * FP8 KV cache.  The Tiny-vLLM summary ("[Hacker News 요약] C++와 CUDA로 vLLM의

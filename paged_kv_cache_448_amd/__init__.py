@@ -11,6 +11,8 @@ Names mirror the C ABI in include/pkv.h and include/pkv_alloc.h:
 * ``paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
 * ``append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
   context_lens, scale, out)`` -- both in one launch (one decode step of one layer)
+* ``paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out)`` --
+  causal attention of the new tokens of every sequence (packed rows) over its paged context
 * ``kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale)`` and
   ``paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, out)``
   -- the same over FP8 (E4M3) pools (uint8 tensors, see ``new_cache_fp8``)
@@ -29,7 +31,7 @@ from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
 
 __all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes",
            "decode_supported", "plan_partition", "new_cache", "new_cache_fp8", "cache_dims", "kv_append_fp8",
-           "paged_attn_decode_fp8", "BlockAllocator", "PkvError", "lib"]
+           "paged_attn_decode_fp8", "paged_prefill", "BlockAllocator", "PkvError", "lib"]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
 IMPLS = {"auto": 0, "simt": 1, "mfma": 2}
@@ -198,6 +200,42 @@ def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
         _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
         _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
+    return out
+
+
+def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out=None, *,
+                  max_query_len, max_context_len=None):
+    """Causal attention of the new tokens of every sequence over its paged context.
+
+    q: [T, Hq, D], sequence i's new tokens at rows query_start[i] .. query_start[i+1]-1
+    (query_start: int32 [B + 1] on the device); context_lens: int32 [B], each L_i
+    counting the new tokens, which are the last n_i positions; max_query_len: host
+    bound of every n_i; max_context_len: host bound of every L_i (default M * block_size).
+    Returns ``out`` ([T, Hq, D])."""
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(q, "q", k_cache.dtype, 3)
+    T, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    _device_tensor(k_cache, "k_cache")
+    _device_tensor(v_cache, "v_cache")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    B = int(block_tables.shape[0])
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    _device_tensor(query_start, "query_start", torch.int32, 1)
+    _need(query_start.shape[0] == B + 1, "query_start must have num_seqs + 1 entries")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    check(lib().pkv_paged_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens),
+                                  _ptr(query_start), T, int(max_query_len), int(max_context_len), ctypes.c_float(scale),
+                                  _ptr(out), B, Hq, Hkv, D, bs, N, _dtype_code(q), _stream(q)))
     return out
 
 

@@ -27,6 +27,8 @@ PROTOTYPES = {
                                                 _vp]),
     "pkv_decode_plan_partition": (_i32, [_i32] * 4),
     "pkv_decode_supported": (_c.c_int, [_i32] * 4),
+    "pkv_paged_prefill": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _c.c_float, _vp, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_kv_append_fp8": (_c.c_int, [_vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _c.c_float,
                                      _c.c_float, _vp]),
     "pkv_paged_attn_decode_fp8": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _c.c_float,

@@ -292,6 +292,46 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                                   stream);
 }
 
+int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
+                      int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale, void* out,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t dtype, hipStream_t stream) {
+  if (num_seqs < 0 || num_tokens < 0 || max_query_len < 0 || max_context_len < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PKV_E_SHAPE;
+  if (num_q_heads % num_kv_heads) return PKV_E_SHAPE;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return PKV_E_SHAPE;
+  if (!dtype_ok(dtype) || !block_size_ok(block_size) || !pkv::mfma_supported(dtype, head_dim, num_q_heads / num_kv_heads))
+    return PKV_E_UNSUPPORTED;
+  if (static_cast<int64_t>(num_blocks) * num_kv_heads * (block_size / 16) > INT_MAX) return PKV_E_SHAPE;
+  if (num_seqs == 0 || num_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start || !out) return PKV_E_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_E_SHAPE;
+  pkv::PrefillParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_cache = static_cast<const uint16_t*>(k_cache);
+  p.v_cache = static_cast<const uint16_t*>(v_cache);
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.query_start = query_start;
+  p.out = static_cast<uint16_t*>(out);
+  p.num_seqs = num_seqs;
+  p.num_tokens = num_tokens;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_context_len = max_context_len;
+  p.max_query_len = max_query_len;
+  p.chunks = 0;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * kLog2e);
+  return pkv::launch_prefill_mfma(p, dtype, stream) == hipSuccess ? PKV_OK : PKV_E_HIP;
+}
+
 int pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                       void* k_cache, void* v_cache, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                       int32_t head_dim, int32_t src_dtype, float k_scale, float v_scale, hipStream_t stream) {

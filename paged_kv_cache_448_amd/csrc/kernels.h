@@ -55,6 +55,22 @@ struct DecodeParams {
   float out_scale;               // factor on every output (FP8 pools: the V scale; else 1)
 };
 
+// Paged prefill: the new tokens of every sequence, packed (sequence i's at rows
+// query_start[i] .. query_start[i+1]-1), attend causally over the paged context.
+struct PrefillParams {
+  const uint16_t* q;             // [T, Hq, D]
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;   // [B, max_blocks_per_seq]
+  const int32_t* context_lens;   // [B]
+  const int32_t* query_start;    // [B + 1]
+  uint16_t* out;                 // [T, Hq, D]
+  int32_t num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
+  int32_t max_blocks_per_seq, max_context_len, max_query_len;
+  int32_t chunks;                // work chunks per (sequence, kv head); set by the launcher
+  float scale_log2;              // softmax scale * log2(e)
+};
+
 // Most tokens one decode workgroup takes (both kernels); longer contexts are
 // always split.  The MFMA kernel's waves hold the pool index of each of their
 // 16-token sub-tiles in one lane each: 8 waves x 64 lanes x 16 tokens.
@@ -73,6 +89,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, hipStream_t stre
 
 // FP8 (E4M3) pools (k_cache / v_cache hold one code per element); no fused append.
 hipError_t launch_decode_fp8(const DecodeParams& p, int dtype, hipStream_t stream);
+
+hipError_t launch_prefill_mfma(const PrefillParams& p, int dtype, hipStream_t stream);
 
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream);
 

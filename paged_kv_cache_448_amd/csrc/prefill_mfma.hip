@@ -1,0 +1,277 @@
+// Paged prefill attention on the matrix cores (MFMA) of gfx950.
+//
+// Prefill takes all new tokens of a prompt in one pass and is bound by matrix
+// products ("vLLM -- PagedAttention으로 ...", section "Prefill vs Decode");
+// every new token attends causally -- to itself and to earlier positions only
+// ("[Hacker News 요약] ... 'Tiny-vLLM' 직접 구축하기", section "고성능 추론을
+// 위한 고급 최적화 기법") -- over K/V read from the paged pool through the
+// sequence's block table, GQA as in decode.  Sequence i's n_i new tokens are
+// its last n_i context positions: new token j is position L_i - n_i + j, and
+// the positions before the new ones are a prefix already in the pool (a cached
+// prompt prefix or an earlier chunk).
+//
+// Tiles: the same 16x16 MFMA tiles as the decode kernel, with the 16 columns
+// now (new-token position, q head) pairs: column c of a column group is q head
+// kvh*G + c % G of the group's position c / G, so a group covers 16 / G
+// positions.  A wave owns CG consecutive column groups and walks the key
+// sub-tiles (16 keys) from key 0 up to its last position, each sub-tile loaded
+// once (the decode kernel's buffer loads, S in flight) and used by all CG
+// groups:
+//
+//   S^T[16 keys x 16 cols] = K . Q^T    (D/32 mfma 16x16x32 per group)
+//   O^T[D x 16 cols]      += V^T . P^T  (D/16 mfma 16x16x16 per group)
+//
+// Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
+// as in decode.  A key is visible to a column when it is not after the
+// column's position; sub-tiles entirely before the wave's first position need
+// no mask.  Every wave sees every key its columns need, so nothing is combined
+// across waves: each lane divides and stores its columns' outputs itself.
+//
+// Work items: (sequence, kv head, chunk of NW * CG * 16/G new tokens), the
+// chunks of a sequence in descending order so the long causal rows start
+// first.  Items past a sequence's new tokens return at once.
+#include "decode_mfma_kernel.h"
+
+namespace pkv {
+
+namespace {
+
+// Column groups per wave: four at head_dim 64, two at 128 (accumulators of
+// 64 VGPRs either way).
+template <int D> struct PrefillShape;
+template <> struct PrefillShape<64> { static constexpr int kGroups = 4, kDepth = 2; };
+template <> struct PrefillShape<128> { static constexpr int kGroups = 2, kDepth = 2; };
+
+constexpr int kPrefillWaves = 4;
+
+template <typename T, int D, int G, int NW, int CG, int S>
+__global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillParams p) {
+  constexpr int JK = D / 32, JV = D / 16;
+  constexpr int QPC = 16 / G;       // positions per column group
+  constexpr int QPW = CG * QPC;     // positions per wave
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, kg = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  int it = blockIdx.x;
+  const int kvh = it % p.num_kv_heads;
+  it /= p.num_kv_heads;
+  const int chunk = p.chunks - 1 - it % p.chunks;
+  const int seq = it / p.chunks;
+
+  const int s0 = p.query_start[seq];
+  const int n = p.query_start[seq + 1] - s0;
+  const int first = (chunk * NW + wv) * QPW;  // index of the wave's first new token
+  if (s0 < 0 || n <= 0 || s0 + n > p.num_tokens || first >= n) return;
+  const int L = p.context_lens[seq];
+
+  // column (cg, r): new token first + cg*QPC + r/G, q head kvh*G + r%G
+  const int head = kvh * G + r % G;
+  int idx[CG];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) idx[cg] = first + cg * QPC + r / G;
+
+  const bool bad_len = L < n || L > p.max_context_len ||
+                       static_cast<int64_t>(L) > static_cast<int64_t>(p.max_blocks_per_seq) * p.block_size ||
+                       n > p.max_query_len;
+  if (bad_len) {
+    if (kg == 0) {
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (idx[cg] >= n) continue;
+        uint16_t* o = p.out + (static_cast<size_t>(s0 + idx[cg]) * p.num_q_heads + head) * D;
+        for (int d = 0; d < D; ++d) o[d] = kNanBits<T>;
+      }
+    }
+    return;
+  }
+
+  const int p0 = L - n;                          // position of new token 0
+  const int last_tok = min(first + QPW, n) - 1;  // the wave's last new token
+  const int nsub = (p0 + last_tok + 1 + 15) >> 4;
+  const int unmasked = (p0 + first + 1) >> 4;    // sub-tiles before this are visible to every column
+
+  int pos[CG];
+  u32x4 qop[CG][JK];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    const int t = min(idx[cg], n - 1);  // columns past the last new token repeat it (not stored)
+    pos[cg] = p0 + t;
+    const uint16_t* qr = p.q + (static_cast<size_t>(s0 + t) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int j = 0; j < JK; ++j) qop[cg][j] = *reinterpret_cast<const u32x4*>(qr + (kg + 4 * j) * 8);
+  }
+
+  // pool index of sub-tiles win .. win+63, one per lane (-1: a block id outside the pool)
+  int tid = 0, win = -1;
+  bool bad = false;
+  auto fetch_window = [&](int base) {
+    const int k = base + lane;
+    tid = 0;
+    if (k < nsub) {
+      const int tok0 = 16 * k;
+      const int blk = tok0 / p.block_size;
+      const int phys = p.block_tables[static_cast<size_t>(seq) * p.max_blocks_per_seq + blk];
+      tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
+                ? (phys * p.num_kv_heads + kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
+                : -1;
+    }
+    win = base;
+  };
+
+  const int last = nsub - 1;
+  const int koff = (r * D + kg * 8) * 2;
+  const int voff = (4 * kg * D + r * JV) * 2;
+  auto load = [&](int k, Tile<D>& t) {
+    const int kk = min(k, last);
+    if ((kk & ~63) != win) fetch_window(kk & ~63);
+    int sub = __builtin_amdgcn_readlane(tid, kk & 63);
+    bad |= sub < 0;
+    sub = max(sub, 0);
+    const uint16_t* kt = p.k_cache + static_cast<size_t>(sub) * (16 * D);
+    const uint16_t* vt = p.v_cache + static_cast<size_t>(sub) * (16 * D);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kt), 0, -1, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vt), 0, -1, kBufferConfig);
+#pragma unroll
+    for (int j = 0; j < JK; ++j)
+      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 64 * j, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
+  };
+
+  float m[CG], l[CG];
+  f32x4 o[CG][JV];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    m[cg] = -INFINITY;
+    l[cg] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  auto compute = [&](int k, Tile<D>& t) {
+    const int key0 = 16 * k;
+    u32x2 vop[JV];
+#pragma unroll
+    for (int j = 0; j < JV; ++j) vop[j] = v_operand<D>(t.v, j);
+    if (key0 + 16 > L) {
+      // keys past the context (the last block's tail) may hold anything: zero their V
+      const int nvalid = L - key0;
+      const uint32_t m0 = (4 * kg < nvalid ? 0xffffu : 0u) | (4 * kg + 1 < nvalid ? 0xffff0000u : 0u);
+      const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < JV; ++j) {
+        vop[j].x &= m0;
+        vop[j].y &= m1;
+      }
+    }
+    const bool masked = k >= unmasked;
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[cg][j], sc);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = sc[i] * p.scale_log2;
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = key0 + 4 * kg + i <= pos[cg] ? x[i] : -INFINITY;
+      }
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = max_xor32(max_xor16(bm));
+      const float mn = fmaxf(m[cg], bm);
+      const float al = fast_exp2(m[cg] - mn);
+      m[cg] = mn;
+      const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
+      const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
+      l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg] * al));
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < JV; ++j) o[cg][j] *= al;
+      }
+      const u32x2 pop = {p01, p23};
+#pragma unroll
+      for (int j = 0; j < JV; ++j) o[cg][j] = Mma<T>::pv(vop[j], pop, o[cg][j]);
+    }
+  };
+
+  {
+    Tile<D> t[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) load(i, t[i]);
+    const int n_pad = (nsub + S - 1) / S * S;
+    int kb = 0;
+    for (; kb + S < n_pad; kb += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        compute(kb + i, t[i]);
+        load(kb + i + S, t[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (kb + i < nsub) compute(kb + i, t[i]);
+  }
+
+  // lane (kg, r) holds rows 4kg+i of O^T for column r: dims (4kg+i)*JV + j
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    float lt = add_xor32(add_xor16(l[cg]));
+    if (bad) lt = __int_as_float(0x7fc00000);
+    const float inv = 1.f / lt;
+    if (idx[cg] >= n) continue;
+    uint16_t* orow = p.out + (static_cast<size_t>(s0 + idx[cg]) * p.num_q_heads + head) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t w[JV / 2];
+#pragma unroll
+      for (int j = 0; j < JV / 2; ++j)
+        w[j] = static_cast<uint32_t>(to_bits<T>(o[cg][2 * j][i] * inv)) |
+               (static_cast<uint32_t>(to_bits<T>(o[cg][2 * j + 1][i] * inv)) << 16);
+      uint16_t* dst = orow + (4 * kg + i) * JV;
+      if constexpr (JV == 4) {
+        *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
+      } else {
+        *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  }
+}
+
+template <typename T, int D, int G>
+hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
+  constexpr int CG = PrefillShape<D>::kGroups, S = PrefillShape<D>::kDepth, NW = kPrefillWaves;
+  const int per_wg = NW * CG * (16 / G);
+  PrefillParams q = p;
+  q.chunks = (p.max_query_len + per_wg - 1) / per_wg;
+  const int64_t items = static_cast<int64_t>(p.num_seqs) * q.chunks * p.num_kv_heads;
+  if (items == 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S>), dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
+                     0, stream, q);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_g(const PrefillParams& p, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_t<T, D, 1>(p, stream);
+    case 2: return launch_t<T, D, 2>(p, stream);
+    case 4: return launch_t<T, D, 4>(p, stream);
+    case 8: return launch_t<T, D, 8>(p, stream);
+    case 16: return launch_t<T, D, 16>(p, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillParams& p, int dtype, hipStream_t stream) {
+  const int group = p.num_q_heads / p.num_kv_heads;
+  if (p.head_dim == 64) return dtype == 0 ? launch_g<Bf16, 64>(p, group, stream) : launch_g<Fp16, 64>(p, group, stream);
+  return dtype == 0 ? launch_g<Bf16, 128>(p, group, stream) : launch_g<Fp16, 128>(p, group, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,161 @@
+"""Paged prefill on the GPU against the prefill oracle (oracle.prefill), within the
+decode tolerance |gpu - oracle| <= 1e-2 + 1e-2 |oracle|.
+
+Each case is a seeded pool holding every sequence's context (workloads.custom),
+NaN in tail slots and unused blocks; the new tokens' K/V are appended by each
+side's own kv_append (the multi-token append), then every new token attends
+causally over its context.  At the benchmark's size the oracle computes sampled
+rows one by one: a new token at position p is the decode of its query over a
+context of p + 1 positions (the equivalence the oracle's pins establish).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_448_amd as pkv
+import workloads
+from gpu_harness import assert_parity, poison_tails_gpu, poison_tails_oracle, to_bits, to_dev
+from oracle.prefill import prefill as oracle_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _new_slots(wl, new):
+    """Slots of the last new[i] context positions of every sequence, in row order."""
+    bs = wl.cfg.block_size
+    out = []
+    for i, (L, n) in enumerate(zip(wl.context_lens, new)):
+        pos = np.arange(int(L) - n, int(L), dtype=np.int64)
+        out.append(wl.block_tables[i, pos // bs].astype(np.int64) * bs + pos % bs)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def _setup(Hq, Hkv, D, bs, lens, new, dtype, seed):
+    wl = workloads.custom(Hq, Hkv, D, bs, lens, dtype, seed=seed)
+    rng = np.random.default_rng(seed + 101)
+    T = int(sum(new))
+    q = workloads.random_bits(rng, (T, Hq, D), dtype)
+    k_new = workloads.random_bits(rng, (T, Hkv, D), dtype)
+    v_new = workloads.random_bits(rng, (T, Hkv, D), dtype)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    return wl, q, k_new, v_new, qs, _new_slots(wl, new)
+
+
+def _gpu(wl, q, k_new, v_new, qs, slots, max_query_len, lens=None, tables=None):
+    c = wl.cfg
+    shape = (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    ly = wl.layers[0]
+    kc, vc = to_dev(ly.k_cache, c.dtype, shape), to_dev(ly.v_cache, c.dtype, shape)
+
+    class _L:  # the two pools, as poison_tails_gpu expects them
+        k_cache, v_cache = kc, vc
+    poison_tails_gpu(wl, _L)
+    if len(slots):
+        pkv.kv_append(to_dev(k_new, c.dtype), to_dev(v_new, c.dtype), torch.from_numpy(slots).cuda(), kc, vc)
+    L = wl.context_lens if lens is None else lens
+    tb = wl.block_tables if tables is None else tables
+    out = pkv.paged_prefill(to_dev(q, c.dtype), kc, vc, torch.from_numpy(tb).cuda(), torch.from_numpy(L).cuda(),
+                            torch.from_numpy(qs).cuda(), c.scale, max_query_len=max_query_len,
+                            max_context_len=int(wl.context_lens.max()))
+    return to_bits(out)
+
+
+def _oracle_pools(wl, k_new, v_new, slots):
+    ly = wl.layers[0]
+    kc, vc = ly.k_cache.copy(), ly.v_cache.copy()
+    poison_tails_oracle(wl, kc, vc)
+    if len(slots):
+        oracle.kv_append(k_new, v_new, slots, kc, vc, num_blocks=wl.num_blocks, block_size=wl.cfg.block_size)
+    return kc, vc
+
+
+CASES = {
+    "tiny": (4, 2, 64, 16, [5, 37], [5, 20], "bf16"),
+    "llama-prompts": (32, 8, 64, 16, [128, 700, 2048, 1, 16, 17, 33], [128, 300, 2048, 1, 16, 1, 17], "bf16"),
+    "fp16-d128-g8": (16, 2, 128, 16, [1000, 257], [1000, 64], "fp16"),
+    "bf16-d128-mha": (8, 8, 128, 32, [300, 77], [300, 77], "bf16"),
+    "bf16-g16-bs256": (16, 1, 64, 256, [600, 5], [250, 5], "bf16"),
+    "fp16-g2-empty-seq": (4, 2, 64, 16, [40, 50, 60], [10, 0, 60], "fp16"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_parity(name):
+    Hq, Hkv, D, bs, lens, new, dtype = CASES[name]
+    wl, q, k_new, v_new, qs, slots = _setup(Hq, Hkv, D, bs, lens, new, dtype, seed=len(name))
+    kc, vc = _oracle_pools(wl, k_new, v_new, slots)
+    c = wl.cfg
+    ref = oracle_prefill(q, kc, vc, wl.block_tables, wl.context_lens, qs, c.scale, dtype=dtype,
+                         num_blocks=wl.num_blocks, num_kv_heads=Hkv, block_size=bs)
+    for mql in (max(new), max(new) + 37):  # a grid larger than needed changes nothing
+        got = _gpu(wl, q, k_new, v_new, qs, slots, mql)
+        r, e = assert_parity(got, ref, dtype, f"{name} max_query_len {mql}")
+        print(f"{name} max_query_len {mql}: max|err| {e:.2e} (ratio {r:.3f})", flush=True)
+
+
+def test_prefill_invalid_sequences_give_nan_only_in_their_rows():
+    Hq, Hkv, D, bs, lens, new, dtype = CASES["tiny"]
+    wl, q, k_new, v_new, qs, slots = _setup(Hq, Hkv, D, bs, lens, new, dtype, seed=3)
+    kc, vc = _oracle_pools(wl, k_new, v_new, slots)
+    c = wl.cfg
+    ref = oracle_prefill(q, kc, vc, wl.block_tables, wl.context_lens, qs, c.scale, dtype=dtype,
+                         num_blocks=wl.num_blocks, num_kv_heads=Hkv, block_size=bs)
+    from oracle.numerics import bits_to_f64
+    lens = wl.context_lens.copy()
+    lens[0] = 3  # fewer context positions than new tokens
+    got = _gpu(wl, q, k_new, v_new, qs, slots, max(new), lens=lens)
+    assert np.all(np.isnan(bits_to_f64(got[:5], dtype)))
+    assert_parity(got[5:], ref[5:], dtype, "valid sequence next to an invalid one")
+    tables = wl.block_tables.copy()
+    tables[1, 0] = wl.num_blocks  # first block of sequence 1 outside the pool
+    got = _gpu(wl, q, k_new, v_new, qs, slots, max(new), tables=tables)
+    assert np.all(np.isnan(bits_to_f64(got[5:], dtype)))
+    assert_parity(got[:5], ref[:5], dtype, "valid sequence next to a bad block id")
+
+
+def test_prefill_rejects_bad_arguments():
+    kc = pkv.new_cache(4, 2, 16, 64)
+    q = torch.zeros((3, 4, 64), dtype=torch.bfloat16, device="cuda")
+    t = torch.zeros((1, 4), dtype=torch.int32, device="cuda")
+    lens = torch.full((1,), 3, dtype=torch.int32, device="cuda")
+    qs = torch.tensor([0, 3], dtype=torch.int32, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_prefill(q, kc, kc.clone(), t, lens, qs[:1], 0.125, max_query_len=3)
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_prefill(q, kc, kc.clone(), t, lens, qs, 0.125, max_query_len=3, max_context_len=65)
+    q5 = torch.zeros((3, 6, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_prefill(q5, kc, kc.clone(), t, lens, qs, 0.125, max_query_len=3)
+
+
+def test_prefill_parity_benchmark_batch_sampled():
+    """The benchmark's prompt batch (the Llama-3.2-1B-shaped workload, every context a
+    whole prompt) in the benchmark's launch: sampled rows (first, last and two random
+    new tokens of every sequence) against the decode oracle over p + 1 positions."""
+    wl = workloads.build(2, poison=False)
+    c = wl.cfg
+    lens = wl.context_lens
+    new = [int(x) for x in lens]
+    rng = np.random.default_rng(77)
+    T = int(sum(new))
+    q = workloads.random_bits(rng, (T, c.num_q_heads, c.head_dim), c.dtype)
+    qs = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    shape = (wl.num_blocks, c.num_kv_heads, c.block_size, c.head_dim)
+    ly = wl.layers[0]
+    kc, vc = to_dev(ly.k_cache, c.dtype, shape), to_dev(ly.v_cache, c.dtype, shape)
+    out = pkv.paged_prefill(to_dev(q, c.dtype), kc, vc, torch.from_numpy(wl.block_tables).cuda(),
+                            torch.from_numpy(lens).cuda(), torch.from_numpy(qs).cuda(), c.scale,
+                            max_query_len=max(new), max_context_len=int(lens.max()))
+    got = to_bits(out)
+    rows, seq, ctx = [], [], []
+    for i, L in enumerate(new):
+        for j in sorted({0, L - 1, int(rng.integers(0, L)), int(rng.integers(0, L))}):
+            rows.append(qs[i] + j)
+            seq.append(i)
+            ctx.append(j + 1)  # no prefix: new token j is position j
+    rows = np.array(rows)
+    ref = oracle.decode(q[rows], ly.k_cache, ly.v_cache, wl.block_tables[seq], np.array(ctx), c.scale, dtype=c.dtype,
+                        num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads, block_size=c.block_size)
+    r, e = assert_parity(got[rows], ref, c.dtype, "benchmark batch, sampled rows")
+    print(f"benchmark batch: {len(rows)} sampled rows, max|err| {e:.2e} (ratio {r:.3f})", flush=True)
