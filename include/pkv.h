@@ -234,7 +234,8 @@ int pkv_decode_supported(int32_t impl, int32_t dtype, int32_t head_dim, int32_t 
  *   max_query_len host bound of every n_i (sizes the grid); max_context_len host
  *                 bound of every L_i, at most max_blocks_per_seq * block_size.
  *   out           [num_tokens][num_q_heads][head_dim] in dtype.
- *   the pools, block_tables and scale as in pkv_paged_attn_decode.
+ *   scale         softmax scale, positive and finite.
+ *   the pools and block_tables as in pkv_paged_attn_decode.
  *
  * A sequence with n_i > max_query_len, L_i < n_i or L_i above the bounds gets NaN
  * in its rows (rows past the first max_query_len are not written); a block id

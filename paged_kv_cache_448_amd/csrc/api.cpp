@@ -303,6 +303,7 @@ int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache, c
   if (num_q_heads % num_kv_heads) return PKV_E_SHAPE;
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PKV_E_SHAPE;
+  if (!scale_ok(scale)) return PKV_E_SHAPE;
   if (!dtype_ok(dtype) || !block_size_ok(block_size) || !pkv::mfma_supported(dtype, head_dim, num_q_heads / num_kv_heads))
     return PKV_E_UNSUPPORTED;
   if (static_cast<int64_t>(num_blocks) * num_kv_heads * (block_size / 16) > INT_MAX) return PKV_E_SHAPE;

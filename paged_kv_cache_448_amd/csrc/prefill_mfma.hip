@@ -22,7 +22,9 @@
 //   O^T[D x 16 cols]      += V^T . P^T  (D/16 mfma 16x16x16 per group)
 //
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
-// as in decode.  A key is visible to a column when it is not after the
+// as in decode; the running reference is moved only when a score exceeds it by
+// more than a fixed slack, so most sub-tiles need no rescaling of the
+// accumulators (the result is the same: softmax does not depend on the shift).  A key is visible to a column when it is not after the
 // column's position; sub-tiles entirely before the wave's first position need
 // no mask.  Every wave sees every key its columns need, so nothing is combined
 // across waves: each lane divides and stores its columns' outputs itself.
@@ -30,11 +32,17 @@
 // Work items: (sequence, kv head, chunk of NW * CG * 16/G new tokens), the
 // chunks of a sequence in descending order so the long causal rows start
 // first.  Items past a sequence's new tokens return at once.
+#include <type_traits>
+
 #include "decode_mfma_kernel.h"
 
 namespace pkv {
 
 namespace {
+
+// Headroom of the lazily moved softmax reference, log2 units (probabilities up
+// to 2^8 before the reference catches up; exact in bf16 and fp16).
+constexpr float kRescaleSlack = 8.f;
 
 // Column groups per wave: four at head_dim 64, two at 128 (accumulators of
 // 64 VGPRs either way).
@@ -150,7 +158,8 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillPara
     for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int k, Tile<D>& t) {
+  // causal: std::true_type for sub-tiles that some column must not fully see
+  auto compute = [&](int k, Tile<D>& t, auto causal) {
     const int key0 = 16 * k;
     u32x2 vop[JV];
 #pragma unroll
@@ -166,31 +175,34 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillPara
         vop[j].y &= m1;
       }
     }
-    const bool masked = k >= unmasked;
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[cg][j], sc);
-      float x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = sc[i] * p.scale_log2;
-      if (masked) {
+      float x[4] = {sc[0], sc[1], sc[2], sc[3]};
+      if constexpr (decltype(causal)::value) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = key0 + 4 * kg + i <= pos[cg] ? x[i] : -INFINITY;
       }
+      // the column's maximum, raw, then in log2 units (the scale is positive)
       float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = max_xor32(max_xor16(bm));
-      const float mn = fmaxf(m[cg], bm);
-      const float al = fast_exp2(m[cg] - mn);
-      m[cg] = mn;
-      const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
-      const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
-      l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg] * al));
-      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+      bm = max_xor32(max_xor16(bm)) * p.scale_log2;
+      // lazy rescaling: the reference m moves only when a score exceeds it by
+      // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack
+      const bool up = bm > m[cg] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float mn = up ? bm : m[cg];
+        const float al = fast_exp2(m[cg] - mn);
+        m[cg] = mn;
+        l[cg] *= al;
 #pragma unroll
         for (int j = 0; j < JV; ++j) o[cg][j] *= al;
       }
+      const float nm = -m[cg];
+      const uint32_t p01 = Mma<T>::pack(fast_exp2(fmaf(x[0], p.scale_log2, nm)), fast_exp2(fmaf(x[1], p.scale_log2, nm)));
+      const uint32_t p23 = Mma<T>::pack(fast_exp2(fmaf(x[2], p.scale_log2, nm)), fast_exp2(fmaf(x[3], p.scale_log2, nm)));
+      l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg]));
       const u32x2 pop = {p01, p23};
 #pragma unroll
       for (int j = 0; j < JV; ++j) o[cg][j] = Mma<T>::pv(vop[j], pop, o[cg][j]);
@@ -206,13 +218,17 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillPara
     for (; kb + S < n_pad; kb += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
-        compute(kb + i, t[i]);
+        if (kb + i < unmasked) {
+          compute(kb + i, t[i], std::false_type{});
+        } else {
+          compute(kb + i, t[i], std::true_type{});
+        }
         load(kb + i + S, t[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < S; ++i)
-      if (kb + i < nsub) compute(kb + i, t[i]);
+      if (kb + i < nsub) compute(kb + i, t[i], std::true_type{});
   }
 
   // lane (kg, r) holds rows 4kg+i of O^T for column r: dims (4kg+i)*JV + j

@@ -161,3 +161,24 @@ def _decode_fp8(**kw):
 ])
 def test_decode_fp8_rejects_bad_arguments_before_launch(kw, status):
     assert _decode_fp8(**kw) == status
+
+
+def _prefill(**kw):
+    a = dict(q=16, kc=16, vc=16, bt=16, mb=4, cl=16, qs=16, T=8, mql=8, mcl=64, scale=0.125, out=16, B=2, Hq=4,
+             Hkv=2, D=64, bs=16, N=8, dt=0)
+    a.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return pkv.lib().pkv_paged_prefill(p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]), p(a["qs"]),
+                                       a["T"], a["mql"], a["mcl"], ctypes.c_float(a["scale"]), p(a["out"]), a["B"],
+                                       a["Hq"], a["Hkv"], a["D"], a["bs"], a["N"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=NULL), E_NULL), (dict(qs=NULL), E_NULL), (dict(out=NULL), E_NULL), (dict(cl=NULL), E_NULL),
+    (dict(T=-1), E_SHAPE), (dict(mql=-1), E_SHAPE), (dict(mcl=65), E_SHAPE), (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(scale=0.0), E_SHAPE), (dict(scale=-0.5), E_SHAPE), (dict(scale=float("nan")), E_SHAPE), (dict(q=8), E_SHAPE),
+    (dict(D=96), E_UNSUPPORTED), (dict(dt=3), E_UNSUPPORTED), (dict(Hq=6, Hkv=2), E_UNSUPPORTED),
+    (dict(bs=24), E_UNSUPPORTED), (dict(B=0), OK), (dict(T=0, q=NULL), OK), (dict(mql=0), OK),
+])
+def test_prefill_rejects_bad_arguments_before_launch(kw, status):
+    assert _prefill(**kw) == status
