@@ -378,7 +378,8 @@ def fp8_decode_bytes(wl):
     return (unique16 - small) // c.elem_bytes + small
 
 
-def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale=0.0125, v_scale=0.01):
+def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale=0.0125, v_scale=0.01,
+              schedule="host"):
     """Decode step over FP8 (E4M3) pools (see --kv fp8): per layer, kv_append_fp8 of
     this step's token per sequence, then paged_attn_decode_fp8."""
     import torch
@@ -423,6 +424,7 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
     tables = torch.from_numpy(wl.block_tables).to(dev)
     lens = torch.from_numpy(wl.context_lens).to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    order = torch.from_numpy(pkv.decode_schedule(wl.context_lens)).to(dev) if schedule == "host" else None
     mcl = int(wl.context_lens.max())
     ws = torch.empty(max(pkv.decode_workspace_bytes(B, c.num_q_heads, Hkv, D, bs, mcl), 256), dtype=torch.uint8,
                      device=dev)
@@ -432,7 +434,7 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
 
     def decode(t):
         pkv.paged_attn_decode_fp8(t["q"], t["kc"], t["vc"], tables, lens, c.scale, k_scale, v_scale, t["out"],
-                                  max_context_len=mcl, workspace=ws)
+                                  max_context_len=mcl, workspace=ws, seq_order=order)
 
     def step(i):
         for t in layers[i % R]:
@@ -513,6 +515,7 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
                                   f"sequences, {c.num_layers} layer(s), {c.num_q_heads}q/{Hkv}kv heads, head_dim {D}, "
                                   f"block_size {bs}", "config_id": config, "kv": "fp8_e4m3",
                       "k_scale": k_scale, "v_scale": v_scale, "partition_tokens": part, "rotations": R},
+           "schedule": ("host dispatch order (pkv_decode_schedule)" if order is not None else "sequence order"),
            "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1), "decode_call_us": round(dec_us, 2),
            "decode_bytes_unique": unique,
            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -540,6 +543,8 @@ def main():
     ap.add_argument("--loop", default=None, help="continuous-batching loop workload (e.g. cb-llama3.2-1b)")
     ap.add_argument("--prefill", action="store_true",
                     help="paged prefill of the workload's contexts as whole prompts (TFLOP/s)")
+    ap.add_argument("--schedule", default="host", choices=["host", "none"],
+                    help="host: pass the dispatch order pkv_decode_schedule makes from the lengths; none: sequence order")
     ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
                     help="fp8: the step over FP8 (E4M3) pools (kv_append_fp8 + paged_attn_decode_fp8)")
     args = ap.parse_args()
@@ -556,7 +561,8 @@ def main():
         prefill_bench(args.config, args.steps, args.warmup, args.cpu_budget)
         return
     if args.kv == "fp8" and not args.pmc_summary:
-        fp8_bench(args.config, args.steps, args.warmup, args.cpu_budget, args.copy_calibration)
+        fp8_bench(args.config, args.steps, args.warmup, args.cpu_budget, args.copy_calibration,
+                  schedule=args.schedule)
         return
 
     import workloads
@@ -606,6 +612,8 @@ def main():
     lens = torch.from_numpy(wl.context_lens).to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     B = len(wl.context_lens)
+    # dispatch order from the host's copy of the lengths (as the block tables)
+    order = torch.from_numpy(pkv.decode_schedule(wl.context_lens)).to(dev) if args.schedule == "host" else None
     mcl = int(wl.context_lens.max())
     ws_bytes = pkv.decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, mcl,
                                           args.partition)
@@ -616,7 +624,7 @@ def main():
 
     def decode(t):
         pkv.paged_attn_decode(t["q"], t["kc"], t["vc"], tables, lens, c.scale, t["out"], max_context_len=mcl,
-                              workspace=ws, partition_tokens=args.partition, impl=args.impl)
+                              workspace=ws, partition_tokens=args.partition, impl=args.impl, seq_order=order)
 
     fused = not args.unfused
     if fused and not pkv.decode_supported("mfma", c.dtype, c.head_dim, c.group):
@@ -631,7 +639,7 @@ def main():
             if fused:
                 pkv.append_paged_attn_decode(t["q"], t["kn"], t["vn"], slots, t["kc"], t["vc"], tables, lens, c.scale,
                                              t["out"], max_context_len=mcl, workspace=ws,
-                                             partition_tokens=args.partition)
+                                             partition_tokens=args.partition, seq_order=order)
                 continue
             pkv.kv_append(t["kn"], t["vn"], slots, t["kc"], t["vc"])
             if evs is not None:
@@ -788,6 +796,7 @@ def main():
         "decode_only_hbm_frac": None if decode_only_us is None else round(unique / (decode_only_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
         "launch": launch,
         "append": "fused into the decode kernel" if fused else "separate kv_append kernel",
+        "schedule": ("host dispatch order (pkv_decode_schedule)" if order is not None else "sequence order"),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -152,6 +152,17 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
  *                     single pass over longer contexts) are cut to 8192.
  *   impl              PKV_IMPL_AUTO, PKV_IMPL_SIMT (vector-ALU dot products) or
  *                     PKV_IMPL_MFMA (matrix-core tiles).
+ *   seq_order         NULL, or a device array [num_seqs] int32: the dispatch
+ *                     order, a permutation of 0 .. num_seqs-1 (work slot s
+ *                     decodes sequence seq_order[s]); pkv_decode_schedule makes
+ *                     one from the host's copy of the context lengths.  It
+ *                     changes only which workgroup decodes which sequence:
+ *                     outputs stay indexed by sequence and are bit-identical to
+ *                     those without an order.  Not a permutation: the output
+ *                     rows of sequences no slot names are unspecified (entries
+ *                     outside [0, num_seqs) are skipped; a repeated entry
+ *                     decodes its sequence twice); nothing is read or written
+ *                     outside the caller's buffers.
  * Results of all choices agree to fp32 rounding.
  */
 int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_cache,
@@ -160,7 +171,7 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
                              void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                             int32_t impl, hipStream_t stream);
+                             int32_t impl, const int32_t* seq_order, hipStream_t stream);
 
 /*
  * pkv_append_paged_attn_decode -- one decode step of one layer in a single
@@ -176,7 +187,8 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
  *                 sequence".  That slot must lie in no other sequence's
  *                 context (a block manager guarantees it for the block a
  *                 sequence is still filling).
- *   the other arguments are those of pkv_paged_attn_decode_ex (MFMA kernel).
+ *   the other arguments are those of pkv_paged_attn_decode_ex (MFMA kernel),
+ *   seq_order included.
  *
  * Results, when the preconditions hold: the pools and out are bit-identical
  * to pkv_kv_append(k_new, v_new, slot_mapping, B, ...) followed by
@@ -193,7 +205,8 @@ int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v
                                  const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace,
-                                 size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream);
+                                 size_t workspace_bytes, int32_t partition_tokens, const int32_t* seq_order,
+                                 hipStream_t stream);
 
 /*
  * pkv_decode_plan_partition -- the partition size (tokens) the automatic choice
@@ -201,6 +214,27 @@ int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v
  */
 int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t block_size,
                                   int32_t max_context_len);
+
+/*
+ * pkv_decode_schedule -- a dispatch order for the decode calls' seq_order,
+ * computed on the host from the host's copy of the context lengths (a block
+ * manager keeps them: it hands out the block tables).  Host memory only; no
+ * device call.
+ *
+ * The pages fix what decode computes, not how work is spread over the GPU;
+ * this is a scheduling aid that leaves every output bit unchanged.  A launch
+ * gives each of the MI355X's 8 XCDs a contiguous range of work slots; the
+ * order deals the sequences, longest first, each to the XCD group with the
+ * fewest tokens so far that has room (group x holds ceil(B/8) slots for
+ * x < B % 8, floor(B/8) otherwise), and keeps each group longest first, so the
+ * XCDs get about equal work and each starts its long contexts first.
+ *
+ *   context_lens  [num_seqs] int32, host memory (negative values count as 0)
+ *   seq_order     [num_seqs] int32, host memory, written: a permutation of
+ *                 0 .. num_seqs-1.
+ * Errors: PKV_E_SHAPE (num_seqs < 0), PKV_E_NULL.
+ */
+int pkv_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t* seq_order);
 
 /*
  * pkv_decode_supported -- 1 if the decode kernel `impl` (PKV_IMPL_*) is built for
@@ -293,8 +327,9 @@ int pkv_kv_append_fp8(const void* k, const void* v, const int64_t* slot_mapping,
  *
  *   q, out        [num_seqs][num_q_heads][head_dim] in dtype (PKV_BF16 / PKV_FP16).
  *   k_scale, v_scale  positive and finite.
- *   the other arguments are those of pkv_paged_attn_decode_ex; the workspace is
- *   sized by the same pkv_decode_workspace_bytes_ex query.
+ *   the other arguments are those of pkv_paged_attn_decode_ex (seq_order
+ *   included); the workspace is sized by the same pkv_decode_workspace_bytes_ex
+ *   query.
  * Every code is exact in dtype, so the kernel runs the 16-bit MFMA tiles on
  * the widened codes; k_scale is folded into the softmax scale and v_scale
  * into the output (not into any element).  Tails, empty and invalid
@@ -309,7 +344,7 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                              hipStream_t stream);
+                              const int32_t* seq_order, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,8 @@ head, token of the block), K and V alike.
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
@@ -117,14 +119,35 @@ def plan_partition(num_seqs, num_kv_heads, block_size, max_context_len):
     return int(lib().pkv_decode_plan_partition(num_seqs, num_kv_heads, block_size, max_context_len))
 
 
+def decode_schedule(context_lens):
+    """Dispatch order for the decode calls' ``seq_order``, from the host's copy of
+    the context lengths (int sequence or numpy array): longest first, dealt so
+    that the XCDs get about equal work.  Returns an int32 numpy permutation."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    _need(lens.ndim == 1, "context_lens must be one-dimensional")
+    order = np.empty(lens.shape[0], dtype=np.int32)
+    check(lib().pkv_decode_schedule(lens.ctypes.data, int(lens.shape[0]), order.ctypes.data))
+    return order
+
+
+def _order_ptr(seq_order, B):
+    if seq_order is None:
+        return None
+    _device_tensor(seq_order, "seq_order", torch.int32, 1)
+    _need(seq_order.shape[0] == B, "seq_order must have one entry per sequence")
+    return _ptr(seq_order)
+
+
 def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, *,
-                      max_context_len=None, workspace=None, partition_tokens=0, impl="auto"):
+                      max_context_len=None, workspace=None, partition_tokens=0, impl="auto", seq_order=None):
     """softmax(scale q K^T) V per sequence over its paged context.
 
     q: [B, Hq, D]; block_tables: int32 [B, M]; context_lens: int32 [B] (device);
     max_context_len: host-side bound of every length (default M * block_size);
     workspace: uint8 device tensor of at least decode_workspace_bytes(...) bytes
-    (allocated through torch when omitted).  Returns ``out`` ([B, Hq, D]).
+    (allocated through torch when omitted); seq_order: optional int32 [B] device
+    permutation (see decode_schedule), which changes only the work order.
+    Returns ``out`` ([B, Hq, D]).
     """
     N, Hkv, bs, D = cache_dims(k_cache)
     _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
@@ -154,12 +177,13 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     check(lib().pkv_paged_attn_decode_ex(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
         ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N, _dtype_code(q), _ptr(workspace),
-        ctypes.c_size_t(workspace.numel()), int(partition_tokens), IMPLS[impl], _stream(q)))
+        ctypes.c_size_t(workspace.numel()), int(partition_tokens), IMPLS[impl], _order_ptr(seq_order, B),
+        _stream(q)))
     return out
 
 
 def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
-                             out=None, *, max_context_len=None, workspace=None, partition_tokens=0):
+                             out=None, *, max_context_len=None, workspace=None, partition_tokens=0, seq_order=None):
     """kv_append of one token per sequence, then paged_attn_decode, in one launch.
 
     k_new, v_new: [B, Hkv, D]; slot_mapping: int64 [B], the slot of position
@@ -199,7 +223,8 @@ def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
     check(lib().pkv_append_paged_attn_decode(
         _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
         _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
-        _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
+        _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens),
+        _order_ptr(seq_order, B), _stream(q)))
     return out
 
 
@@ -266,7 +291,7 @@ def kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale):
 
 
 def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale, out=None, *,
-                          max_context_len=None, workspace=None, partition_tokens=0):
+                          max_context_len=None, workspace=None, partition_tokens=0, seq_order=None):
     """paged_attn_decode over FP8 pools: K = e4m3(k_cache) * k_scale, V = e4m3(v_cache) * v_scale.
 
     q (bf16 or fp16) [B, Hq, D]; the pools are uint8 tensors from new_cache_fp8;
@@ -300,7 +325,8 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale
     check(lib().pkv_paged_attn_decode_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
         ctypes.c_float(scale), _scale(k_scale, "k_scale"), _scale(v_scale, "v_scale"), _ptr(out), B, Hq, Hkv, D, bs,
-        N, code, _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _stream(q)))
+        N, code, _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens),
+        _order_ptr(seq_order, B), _stream(q)))
     return out
 
 

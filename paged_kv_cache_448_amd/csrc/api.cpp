@@ -1,8 +1,11 @@
 // C-ABI entry points of the paged KV-cache library: argument checks, the
 // partition plan of split-context decode, and kernel launches on the caller's
 // stream.  Nothing here allocates, frees, synchronises or reads device memory.
+#include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <numeric>
+#include <vector>
 
 #include "kernels.h"
 #include "pkv.h"
@@ -21,6 +24,8 @@ bool block_size_ok(int32_t bs) { return bs >= 16 && bs <= 1024 && bs % 16 == 0; 
 
 // Compute units the automatic plan is sized for (MI355X).
 constexpr int64_t kPlanCUs = 256;
+// XCDs the launch's work-item ranges are spread over (MI355X), as in xcd_remap.
+constexpr int kXcds = 8;
 
 // Tokens per partition for the automatic plan, 0 for one pass without merge.
 // One workgroup per (sequence, kv head) reads a whole context when there are
@@ -120,6 +125,39 @@ int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_
   return plan.num_parts > 1 ? plan.part_tokens : 0;
 }
 
+int pkv_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t* seq_order) {
+  if (num_seqs < 0) return PKV_E_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens || !seq_order) return PKV_E_NULL;
+  // Longest context first (ties: lower index first) ...
+  std::vector<int32_t> by_len(num_seqs);
+  std::iota(by_len.begin(), by_len.end(), 0);
+  std::stable_sort(by_len.begin(), by_len.end(),
+                   [&](int32_t a, int32_t b) { return context_lens[a] > context_lens[b]; });
+  // ... each to the XCD group with the fewest tokens so far that still has
+  // room.  Group x holds the work slots the launch's x-th contiguous range of
+  // items covers (xcd_remap): ceil(B/8) slots for the first B % 8 groups,
+  // floor(B/8) for the others.  Within a group the sequences keep the
+  // longest-first order, so each XCD starts its long contexts first.
+  std::vector<std::vector<int32_t>> groups(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  const int32_t base = num_seqs / kXcds, extra = num_seqs % kXcds;
+  for (const int32_t s : by_len) {
+    int best = -1;
+    for (int g = 0; g < kXcds; ++g) {
+      const int32_t cap = base + (g < extra ? 1 : 0);
+      if (static_cast<int32_t>(groups[g].size()) >= cap) continue;
+      if (best < 0 || load[g] < load[best]) best = g;
+    }
+    groups[best].push_back(s);
+    load[best] += context_lens[s] > 0 ? context_lens[s] : 0;
+  }
+  int32_t k = 0;
+  for (const auto& g : groups)
+    for (const int32_t s : g) seq_order[k++] = s;
+  return PKV_OK;
+}
+
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                      int32_t partition_tokens) {
@@ -158,7 +196,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace, size_t workspace_bytes,
                 int32_t partition_tokens, int32_t impl, const FusedAppend& app, const Fp8Scales* fp8,
-                hipStream_t stream) {
+                const int32_t* seq_order, hipStream_t stream) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_E_SHAPE;
@@ -228,6 +266,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.k_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   p.v_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   p.append_wgs = 0;  // set by the MFMA launcher for fused calls
+  p.seq_order = seq_order;
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -260,10 +299,11 @@ int pkv_paged_attn_decode_ex(const void* q, const void* k_cache, const void* v_c
                              void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
                              void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                             int32_t impl, hipStream_t stream) {
+                             int32_t impl, const int32_t* seq_order, hipStream_t stream) {
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
-                     workspace_bytes, partition_tokens, impl, FusedAppend{nullptr, nullptr, nullptr}, nullptr, stream);
+                     workspace_bytes, partition_tokens, impl, FusedAppend{nullptr, nullptr, nullptr}, nullptr,
+                     seq_order, stream);
 }
 
 int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v_new,
@@ -272,12 +312,13 @@ int pkv_append_paged_attn_decode(const void* q, const void* k_new, const void* v
                                  const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace,
-                                 size_t workspace_bytes, int32_t partition_tokens, hipStream_t stream) {
+                                 size_t workspace_bytes, int32_t partition_tokens, const int32_t* seq_order,
+                                 hipStream_t stream) {
   if (num_seqs > 0 && !slot_mapping) return PKV_E_NULL;
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping},
-                     nullptr, stream);
+                     nullptr, seq_order, stream);
 }
 
 int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -289,7 +330,7 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
   return pkv_paged_attn_decode_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                                   max_context_len, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                   block_size, num_blocks, dtype, workspace, workspace_bytes, 0, PKV_IMPL_AUTO,
-                                  stream);
+                                  nullptr, stream);
 }
 
 int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -368,12 +409,12 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                              hipStream_t stream) {
+                              const int32_t* seq_order, hipStream_t stream) {
   const Fp8Scales sc{k_scale, v_scale};
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{nullptr, nullptr, nullptr}, &sc,
-                     stream);
+                     seq_order, stream);
 }
 
 }  // extern "C"

@@ -18,9 +18,12 @@ struct WorkItem {
   int seq, kvh, part;
 };
 
-// Items are ordered (sequence, partition, kv head); see xcd_remap for the
-// workgroup -> item order.  bid / n: this workgroup's index among the n
-// decode workgroups of the launch.
+// Items are ordered (work slot, partition, kv head); see xcd_remap for the
+// workgroup -> item order.  Work slot s is sequence s, or seq_order[s] when
+// the caller passes a dispatch order (a host schedule that balances the XCDs'
+// work and starts long contexts first).  bid / n: this workgroup's index among
+// the n decode workgroups of the launch.  An order entry outside
+// [0, num_seqs) gives seq = -1: the workgroup does nothing.
 __device__ __forceinline__ WorkItem decode_item(const DecodeParams& p, int bid, int n) {
   int it = xcd_remap(bid, n);
   WorkItem w;
@@ -28,6 +31,10 @@ __device__ __forceinline__ WorkItem decode_item(const DecodeParams& p, int bid, 
   it /= p.num_kv_heads;
   w.part = it % p.num_parts;
   w.seq = it / p.num_parts;
+  if (p.seq_order != nullptr) {
+    const int s = p.seq_order[w.seq];
+    w.seq = static_cast<unsigned>(s) < static_cast<unsigned>(p.num_seqs) ? s : -1;
+  }
   return w;
 }
 

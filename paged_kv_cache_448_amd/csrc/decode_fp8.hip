@@ -98,17 +98,19 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int r = lane & 15, kg = lane >> 4;
   const WorkItem w = decode_item(p, blockIdx.x, gridDim.x);
+  if (w.seq < 0) return;
   const int L = p.context_lens[w.seq];
+  const bool bad_len = bad_length(L, p);
+  if (bad_len || L == 0) {
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len);
+    return;
+  }
   const int start = w.part * p.part_tokens;
-
-  // Block-table window, read together with the context length (it does not
-  // depend on it): lane k holds the entry of this wave's k-th sub-tile of the
-  // partition for every k the table row can hold; entries past the context are
-  // never used.
-  const int tok0 = start + 16 * (wv + lane * NW);
-  const int blk0 = tok0 / p.block_size;
-  int tab = -1;
-  if (blk0 < p.max_blocks_per_seq) tab = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk0];
+  if (start >= L) return;
+  const int end = min(L, start + p.part_tokens);
+  const int nsub = (end - start + 15) >> 4;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
 
   // Q^T operand: column r = q head kvh*G + r (zero for r >= G), dims of run kg + 4j
   u32x4 qop[JK];
@@ -122,23 +124,15 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
     }
   }
 
-  const bool bad_len = bad_length(L, p);
-  if (bad_len || L == 0) {
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len);
-    return;
-  }
-  if (start >= L) return;
-  const int end = min(L, start + p.part_tokens);
-  const int nsub = (end - start + 15) >> 4;
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
-  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
-
-  // lane k < n_w: pool index of this wave's k-th sub-tile (16*D codes), or -1
-  // for a block id outside the pool
+  // lane k: pool index of this wave's k-th sub-tile (16*D codes), or -1 for a
+  // block id outside the pool
   int tid = 0;
   if (lane < n_w) {
-    tid = static_cast<unsigned>(tab) < static_cast<unsigned>(p.num_blocks)
-              ? (tab * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk0 * p.block_size) >> 4)
+    const int tok0 = start + 16 * (wv + lane * NW);
+    const int blk = tok0 / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
+    tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
+              ? (phys * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
               : -1;
   }
   bool bad = false;

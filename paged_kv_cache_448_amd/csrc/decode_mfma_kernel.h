@@ -175,6 +175,7 @@ template <typename T, int D, int G, int NW, int S, int MINW>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
 decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
+  static_assert(NW * kWave >= D, "one thread per dimension stages the appended token");
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -185,18 +186,22 @@ decode_mfma_kernel(DecodeParams p) {
     return;
   }
   const WorkItem w = decode_item(p, blockIdx.x - p.append_wgs, gridDim.x - p.append_wgs);
+  if (w.seq < 0) return;
   const int L = p.context_lens[w.seq];
+  const bool bad_len = bad_length(L, p);
+  if (bad_len || L == 0) {
+    // an appended token needs a position: L = 0 with a slot is a caller error
+    const bool orphan = p.slot_mapping != nullptr && p.slot_mapping[w.seq] >= 0;
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan);
+    return;
+  }
   const int start = w.part * p.part_tokens;
-
-  // Block-table window: lane k reads the entry of this wave's k-th sub-tile of
-  // the partition, for every k the table row can hold.  It does not depend on
-  // the context length, so the length and the window are read in the same
-  // round trip and the first sub-tile loads follow one round trip after the
-  // start; entries past the context are read as plain integers and never used.
-  const int tok0 = start + 16 * (wv + lane * NW);
-  const int blk0 = tok0 / p.block_size;
-  int tab = -1;
-  if (blk0 < p.max_blocks_per_seq) tab = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk0];
+  if (start >= L) return;
+  const int end = min(L, start + p.part_tokens);
+  const int nsub = (end - start + 15) >> 4;
+  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  // this wave owns sub-tiles wv + k*NW, k = 0 .. n_w-1
+  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
 
   // Q^T operand: column r = q head kvh*G + r (zero for r >= G), dims of run kg + 4j
   u32x4 qop[JK];
@@ -210,77 +215,69 @@ decode_mfma_kernel(DecodeParams p) {
     }
   }
 
-  // K and V of the token appended this step (fused append, below), read in
-  // the same round trip: lane c < D/8 holds K dims 8c .. 8c+7, lane c < 16 the
-  // V dims of row slice c.
+  // K and V of the token appended this step (fused append, below); read
+  // before the block-table window so that both are in flight together.
+  // The slot and the physical block of position L-1 are read here too, so the
+  // check below costs no round trip of its own.
   u32x4 krun = {0u, 0u, 0u, 0u};
-  VSlice<D> vrun{};
+  uint16_t vnew = 0;
   int64_t app_slot = -1;
+  int app_phys = 0;
   if (p.slot_mapping != nullptr) {
     const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
-    krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(lane, D / 8 - 1));
-    vrun = *reinterpret_cast<const VSlice<D>*>(p.v_new + row * D + JV * r);
+    const int ti = static_cast<int>(threadIdx.x);
+    krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(ti, D / 8 - 1));
+    vnew = p.v_new[row * D + min(ti, D - 1)];
     app_slot = p.slot_mapping[w.seq];
+    app_phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + (L - 1) / p.block_size];
   }
 
-  const bool bad_len = bad_length(L, p);
-  if (bad_len || L == 0) {
-    // an appended token needs a position: L = 0 with a slot is a caller error
-    const bool orphan = p.slot_mapping != nullptr && app_slot >= 0;
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan);
-    return;
-  }
-  if (start >= L) return;
-  const int end = min(L, start + p.part_tokens);
-  const int nsub = (end - start + 15) >> 4;
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
-  // this wave owns sub-tiles wv + k*NW, k = 0 .. n_w-1
-  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
-
-  // lane k < n_w: index of this wave's k-th sub-tile in the pool (sub-tiles of
-  // 16*D elements, numbered (block*Hkv + kvh)*(bs/16) + sub-tile in block), or
-  // -1 when the table names a block outside the pool.
+  // lane k: index of this wave's k-th sub-tile in the pool (sub-tiles of 16*D
+  // elements, numbered (block*Hkv + kvh)*(bs/16) + sub-tile in block), or -1
+  // when the table names a block outside the pool.
   int tid = 0;
   if (lane < n_w) {
-    tid = static_cast<unsigned>(tab) < static_cast<unsigned>(p.num_blocks)
-              ? (tab * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk0 * p.block_size) >> 4)
+    const int tok0 = start + 16 * (wv + lane * NW);
+    const int blk = tok0 / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
+    tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
+              ? (phys * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
               : -1;
   }
   bool bad = false;
 
   // Fused append of the token decoded this step, which sits at position L-1.
-  // The workgroup whose partition holds L-1 checks the slot against the block
-  // the table names for L-1 (the window entry of that sub-tile) and the wave
-  // that reads that sub-tile puts the token into its registers in place of
-  // whatever the load returned, through LDS of its own (no workgroup barrier).
-  // The pool stores themselves are made by the launch's leading append
-  // workgroups (append_tokens).  A slot that is not the slot of L-1 makes the
-  // sequence's output NaN: this workgroup's heads directly, the other
-  // partitions' rows through the merge.
+  // Its K and V were read together with the block-table window, so the
+  // append adds no dependent round trip before the first sub-tile loads.  The
+  // workgroup whose partition holds L-1 stages the token in LDS, and the wave
+  // that reads that sub-tile puts it into its registers in place of whatever
+  // the load returned; the same workgroup stores the token into the pools (the
+  // same bytes kv_append writes) after its sub-tile loop, where nothing waits
+  // for the stores.  A slot that is not the slot of L-1 is not written and makes the
+  // sequence's output NaN (every workgroup of the sequence checks).
   __shared__ __align__(16) uint16_t sm_new[2][D];  // the appended token's K and V
   int app_w = -1, app_k = -1, app_r = 0;           // wave, step and token row that hold it
-  if (p.slot_mapping != nullptr && app_slot >= 0) {
+  if (p.slot_mapping != nullptr) {
     const int app_pos = L - 1;
-    if (app_pos >= start && app_pos < end) {
-      const int s_tok = (app_pos - start) >> 4;
-      app_w = s_tok % NW;
-      app_k = s_tok / NW;
-      app_r = app_pos & 15;
-      if (wv == app_w) {
-        const int phys = __builtin_amdgcn_readlane(tab, app_k);
-        const int off = app_pos - (app_pos / p.block_size) * p.block_size;
-        // a block outside the pool already poisons the sub-tile's load
-        if (static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks) &&
-            app_slot != static_cast<int64_t>(phys) * p.block_size + off)
-          bad = true;
-        if (lane < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * lane]) = krun;
-        if (lane < 16) *reinterpret_cast<VSlice<D>*>(&sm_new[1][JV * lane]) = vrun;
-        // the same wave reads the rows back in its compute step
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int ti = static_cast<int>(threadIdx.x);
+    const int64_t slot = app_slot;
+    const int blk = app_pos / p.block_size;
+    const int phys = app_phys;
+    const int off = app_pos - blk * p.block_size;
+    if (slot >= 0) {
+      if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
+          slot != static_cast<int64_t>(phys) * p.block_size + off) {
+        bad = true;
+      } else if (app_pos >= start && app_pos < end) {
+        app_r = off & 15;
+        if (ti < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * ti]) = krun;
+        if (ti < D) sm_new[1][ti] = vnew;
+        const int s_tok = (app_pos - start) >> 4;
+        app_w = s_tok % NW;
+        app_k = s_tok / NW;
       }
     }
+    __syncthreads();
   }
 
   // Branch-free, so that every path issues the same loads and the compiler's

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_simt_kernel(DecodeParams p)
   const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
   const int tt = lane & 15, kg = lane >> 4;
   const WorkItem w = decode_item(p, blockIdx.x, gridDim.x);
+  if (w.seq < 0) return;
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
   if (bad_len || L == 0) {

@@ -47,6 +47,9 @@ struct DecodeParams {
   uint16_t* k_cache_w;           // the same pools, writable
   uint16_t* v_cache_w;
   int32_t append_wgs;            // leading workgroups that store the appended tokens (fused append), else 0
+  // Dispatch order (optional): work slot s decodes sequence seq_order[s], a
+  // permutation of [0, num_seqs); nullptr = slot s is sequence s.
+  const int32_t* seq_order;
   int32_t num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks;
   int32_t max_blocks_per_seq, max_context_len;
   int32_t part_tokens;           // tokens per partition, a multiple of 16

@@ -181,7 +181,7 @@ class DecodeLoop:
             check(self._lib.pkv_append_paged_attn_decode(
                 _p(q), _p(k), _p(v), _p(self.slots_d), _p(self.k_pools[layer]), _p(self.v_pools[layer]),
                 _p(self.tables_d), M, _p(self.lens_d), lens_max, scale, _p(out), B, lc.num_q_heads, lc.num_kv_heads,
-                lc.head_dim, bs, lc.num_blocks, self.code, _p(self.workspace), ws, 0, sp))
+                lc.head_dim, bs, lc.num_blocks, self.code, _p(self.workspace), ws, 0, None, sp))
         return lens
 
     def finish(self, rid: int):

@@ -51,7 +51,7 @@ def _decode(**kw):
     return pkv.lib().pkv_paged_attn_decode_ex(p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]),
                                               a["mcl"], ctypes.c_float(a["scale"]), p(a["out"]), a["B"], a["Hq"],
                                               a["Hkv"], a["D"], a["bs"], a["N"], a["dt"], p(a["ws"]),
-                                              ctypes.c_size_t(a["wsb"]), a["pt"], a["impl"], None)
+                                              ctypes.c_size_t(a["wsb"]), a["pt"], a["impl"], None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -111,7 +111,7 @@ def _fused(**kw):
     return pkv.lib().pkv_append_paged_attn_decode(
         p(a["q"]), p(a["kn"]), p(a["vn"]), p(a["sm"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]),
         a["mcl"], ctypes.c_float(a["scale"]), p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["N"],
-        a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None)
+        a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -149,7 +149,7 @@ def _decode_fp8(**kw):
     return pkv.lib().pkv_paged_attn_decode_fp8(
         p(a["q"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]), a["mcl"], ctypes.c_float(a["scale"]),
         ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
-        a["N"], a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None)
+        a["N"], a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
