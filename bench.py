@@ -196,7 +196,7 @@ def load_traffic(workload_name):
     return rec["traffic_bytes_per_launch"]
 
 
-def loop_bench(name, steps, warmup, seed=11):
+def loop_bench(name, steps, warmup, seed=11, schedule=True):
     """Sustained decode tokens/s of the continuous-batching loop (see --loop)."""
     import torch
 
@@ -209,7 +209,7 @@ def loop_bench(name, steps, warmup, seed=11):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     most_prompt = max(sum(reqs[r].prompt_len for r in st.admit) for st in plan)
-    loop = DecodeLoop(lc, dev, max_prompt_tokens=most_prompt)
+    loop = DecodeLoop(lc, dev, max_prompt_tokens=most_prompt, schedule=schedule)
     tdt = loop.dtype
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
@@ -267,7 +267,8 @@ def loop_bench(name, steps, warmup, seed=11):
            "avg_batch": round(tokens / steps, 2), "gpu_ms": round(gpu_ms, 3), "host_enqueue_ms": round(host_s * 1e3, 3),
            "host_wait_ms": round(loop.host_wait_s * 1e3, 3),
            "kv_read_gbs": round(kv_bytes / (wall_s * 1e9), 1),
-           "kv_read_frac_of_peak": round(kv_bytes / (wall_s * 1e9) / HBM_PEAK_GBS, 4)}
+           "kv_read_frac_of_peak": round(kv_bytes / (wall_s * 1e9) / HBM_PEAK_GBS, 4),
+           "schedule": "host dispatch order (pkv_decode_schedule)" if schedule else "sequence order"}
     print(json.dumps(rec), flush=True)
 
 
@@ -555,7 +556,7 @@ def main():
         sys.exit(2)
 
     if args.loop:
-        loop_bench(args.loop, args.steps, args.warmup)
+        loop_bench(args.loop, args.steps, args.warmup, schedule=args.schedule == "host")
         return
     if args.prefill:
         prefill_bench(args.config, args.steps, args.warmup, args.cpu_budget)

@@ -10,7 +10,9 @@ see workloads.loop for the plans used in tests and benchmarks):
    (one kv_append per layer for all of them, one slot per token);
 2. every running sequence takes the slot of its next token (append_slots: a
    fresh block whenever the last one is full), and the running batch's block
-   tables, context lengths and slots are copied to the device;
+   tables, context lengths, slots and dispatch order (pkv_decode_schedule of
+   the lengths: the XCDs get equal work, long contexts start first) are copied
+   to the device;
 3. each layer runs one fused append + decode launch;
 4. sequences that are done return their blocks to the pool.  Their blocks may
    be handed out again in the next step; the stream orders the next step's
@@ -47,7 +49,8 @@ def _p(t):
 class DecodeLoop:
     """Pools for every layer, the host allocator, and the per-step staging."""
 
-    def __init__(self, lc, device="cuda", shuffle_seed: int = 1, ring: int = 4, max_prompt_tokens: int = 0):
+    def __init__(self, lc, device="cuda", shuffle_seed: int = 1, ring: int = 4, max_prompt_tokens: int = 0,
+                 schedule: bool = True):
         self.lc = lc
         self.device = torch.device(device)
         self.dtype = _TORCH_DTYPES[lc.dtype]
@@ -66,11 +69,14 @@ class DecodeLoop:
         self.tables_d = torch.empty(B * self.max_blocks, dtype=torch.int32, device=self.device)
         self.lens_d = torch.empty(B, dtype=torch.int32, device=self.device)
         self.slots_d = torch.empty(B, dtype=torch.int64, device=self.device)
+        self.schedule = schedule
+        self.order_d = torch.empty(B, dtype=torch.int32, device=self.device)
         self.prompt_slots_d = torch.empty(self.max_prompt_tokens, dtype=torch.int64, device=self.device)
         pin = dict(pin_memory=True)
         self._ring = [dict(tables=torch.empty(B * self.max_blocks, dtype=torch.int32, **pin),
                            lens=torch.empty(B, dtype=torch.int32, **pin),
                            slots=torch.empty(B, dtype=torch.int64, **pin),
+                           order=torch.empty(B, dtype=torch.int32, **pin),
                            pslots=torch.empty(self.max_prompt_tokens, dtype=torch.int64, **pin),
                            done=None) for _ in range(ring)]
         self._next = 0
@@ -166,6 +172,12 @@ class DecodeLoop:
         self.tables_d[:B * M].copy_(st["tables"][:B * M], non_blocking=True)
         self.lens_d[:B].copy_(st["lens"][:B], non_blocking=True)
         self.slots_d[:B].copy_(st["slots"][:B], non_blocking=True)
+        order = None
+        if self.schedule:
+            o = st["order"][:B].numpy()
+            check(self._lib.pkv_decode_schedule(lens.ctypes.data, B, o.ctypes.data))
+            self.order_d[:B].copy_(st["order"][:B], non_blocking=True)
+            order = _p(self.order_d)
         self._release(st, stream)
         sp = ctypes.c_void_p(stream.cuda_stream)
         qs, kvs = (B, lc.num_q_heads, lc.head_dim), (B, lc.num_kv_heads, lc.head_dim)
@@ -181,7 +193,7 @@ class DecodeLoop:
             check(self._lib.pkv_append_paged_attn_decode(
                 _p(q), _p(k), _p(v), _p(self.slots_d), _p(self.k_pools[layer]), _p(self.v_pools[layer]),
                 _p(self.tables_d), M, _p(self.lens_d), lens_max, scale, _p(out), B, lc.num_q_heads, lc.num_kv_heads,
-                lc.head_dim, bs, lc.num_blocks, self.code, _p(self.workspace), ws, 0, None, sp))
+                lc.head_dim, bs, lc.num_blocks, self.code, _p(self.workspace), ws, 0, order, sp))
         return lens
 
     def finish(self, rid: int):
