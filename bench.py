@@ -380,9 +380,10 @@ def fp8_decode_bytes(wl):
 
 
 def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale=0.0125, v_scale=0.01,
-              schedule="host"):
-    """Decode step over FP8 (E4M3) pools (see --kv fp8): per layer, kv_append_fp8 of
-    this step's token per sequence, then paged_attn_decode_fp8."""
+              schedule="host", fused=True):
+    """Decode step over FP8 (E4M3) pools (see --kv fp8): per layer, the append of this
+    step's token per sequence and paged_attn_decode_fp8, as one launch
+    (append_paged_attn_decode_fp8) or, unfused, kv_append_fp8 and the decode."""
     import torch
 
     import paged_kv_cache_448_amd as pkv
@@ -439,6 +440,11 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
 
     def step(i):
         for t in layers[i % R]:
+            if fused:
+                pkv.append_paged_attn_decode_fp8(t["q"], t["kn"], t["vn"], slots, t["kc"], t["vc"], tables, lens,
+                                                 c.scale, k_scale, v_scale, t["out"], max_context_len=mcl,
+                                                 workspace=ws, seq_order=order)
+                continue
             pkv.kv_append_fp8(t["kn"], t["vn"], slots, t["kc"], t["vc"], k_scale, v_scale)
             decode(t)
 
@@ -512,11 +518,12 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
     rec = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
            "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": f"kv fp8-e4m3, q/out/mfma {c.dtype}", "data": "synthetic",
-           "config": {"workload": f"{c.name} over FP8 (E4M3) pools: kv_append_fp8 + paged_attn_decode_fp8 of {B} "
+           "config": {"workload": f"{c.name} over FP8 (E4M3) pools: FP8 append + paged_attn_decode_fp8 of {B} "
                                   f"sequences, {c.num_layers} layer(s), {c.num_q_heads}q/{Hkv}kv heads, head_dim {D}, "
                                   f"block_size {bs}", "config_id": config, "kv": "fp8_e4m3",
                       "k_scale": k_scale, "v_scale": v_scale, "partition_tokens": part, "rotations": R},
            "schedule": ("host dispatch order (pkv_decode_schedule)" if order is not None else "sequence order"),
+           "append": "fused into the decode kernel" if fused else "separate kv_append_fp8 kernel",
            "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1), "decode_call_us": round(dec_us, 2),
            "decode_bytes_unique": unique,
            "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -547,7 +554,7 @@ def main():
     ap.add_argument("--schedule", default="host", choices=["host", "none"],
                     help="host: pass the dispatch order pkv_decode_schedule makes from the lengths; none: sequence order")
     ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
-                    help="fp8: the step over FP8 (E4M3) pools (kv_append_fp8 + paged_attn_decode_fp8)")
+                    help="fp8: the step over FP8 (E4M3) pools (append + paged_attn_decode_fp8, fused unless --unfused)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -563,7 +570,7 @@ def main():
         return
     if args.kv == "fp8" and not args.pmc_summary:
         fp8_bench(args.config, args.steps, args.warmup, args.cpu_budget, args.copy_calibration,
-                  schedule=args.schedule)
+                  schedule=args.schedule, fused=not args.unfused)
         return
 
     import workloads

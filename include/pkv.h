@@ -346,6 +346,34 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
                               int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
                               const int32_t* seq_order, hipStream_t stream);
 
+/*
+ * pkv_append_paged_attn_decode_fp8 -- one decode step of one layer over FP8
+ * pools in a single launch: pkv_kv_append_fp8 of one new token per sequence
+ * (k_new, v_new [num_seqs][num_kv_heads][head_dim] in dtype, encoded with the
+ * same rule and scales), then pkv_paged_attn_decode_fp8 over contexts that
+ * include it; the slot_mapping contract is that of
+ * pkv_append_paged_attn_decode.  The same one-launch step the 16-bit pools
+ * have; the pages describe the append and the attention as separate steps and
+ * name FP8 only as a future direction ("[Hacker News 요약] C++와 CUDA로 vLLM의
+ * 경량 고성능 LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section "향후 전망").
+ *
+ * Results, when the preconditions hold: pools and out bit-identical to
+ * pkv_kv_append_fp8(k_new, v_new, slot_mapping, B, ..., k_scale, v_scale)
+ * followed by pkv_paged_attn_decode_fp8(...).  A non-negative slot that is not
+ * the slot of position L_i - 1 (or a sequence with L_i = 0 and a slot) writes
+ * nothing and makes sequence i's output NaN.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (also a scale that is not positive and
+ * finite), PKV_E_UNSUPPORTED, PKV_E_WORKSPACE, PKV_E_HIP.
+ */
+int pkv_append_paged_attn_decode_fp8(const void* q, const void* k_new, const void* v_new,
+                                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len, float scale,
+                                     float k_scale, float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                                     const int32_t* seq_order, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

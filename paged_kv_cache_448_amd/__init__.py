@@ -330,4 +330,52 @@ def paged_attn_decode_fp8(q, k_cache, v_cache, block_tables, context_lens, scale
     return out
 
 
+def append_paged_attn_decode_fp8(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
+                                 k_scale, v_scale, out=None, *, max_context_len=None, workspace=None,
+                                 partition_tokens=0, seq_order=None):
+    """kv_append_fp8 of one token per sequence, then paged_attn_decode_fp8, in one launch.
+
+    k_new, v_new: [B, Hkv, D] in q's dtype; slot_mapping: int64 [B], the slot of
+    position context_lens[i] - 1 of sequence i (negative: nothing appended).
+    Same pools and output as the two calls when that holds; a slot that is not
+    that position's slot is not written and makes sequence i's output NaN.
+    """
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(k_cache, "k_cache", torch.uint8)
+    _device_tensor(v_cache, "v_cache", torch.uint8)
+    _device_tensor(q, "q", None, 3)
+    code = _dtype_code(q)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _device_tensor(t, name, q.dtype, 3)
+        _need(tuple(t.shape) == (B, Hkv, D), f"{name} must be [{B}, {Hkv}, {D}], got {tuple(t.shape)}")
+    _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+    _need(slot_mapping.shape[0] == B, "slot_mapping must have one slot per sequence")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    need = decode_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    check(lib().pkv_append_paged_attn_decode_fp8(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
+        _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _scale(k_scale, "k_scale"),
+        _scale(v_scale, "v_scale"), _ptr(out), B, Hq, Hkv, D, bs, N, code, _ptr(workspace),
+        ctypes.c_size_t(workspace.numel()), int(partition_tokens), _order_ptr(seq_order, B), _stream(q)))
+    return out
+
+
 from .allocator import BlockAllocator  # noqa: E402

@@ -35,6 +35,9 @@ PROTOTYPES = {
     "pkv_paged_attn_decode_fp8": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _c.c_float,
                                              _c.c_float, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                                              _c.c_size_t, _i32, _vp, _vp]),
+    "pkv_append_paged_attn_decode_fp8": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float,
+                                                    _c.c_float, _c.c_float, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                    _i32, _vp, _c.c_size_t, _i32, _vp, _vp]),
     "pkv_alloc_create": (_vp, [_i32, _i32, _c.c_uint64]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_add_seq": (_c.c_int, [_vp, _i64, _i32]),

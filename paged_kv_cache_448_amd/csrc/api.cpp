@@ -227,8 +227,8 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
       break;
     default: return PKV_E_UNSUPPORTED;
   }
-  if (fused && !use_mfma) return PKV_E_UNSUPPORTED;  // the append is fused into the MFMA kernel only
-  if (fp8 && (fused || !use_mfma)) return PKV_E_UNSUPPORTED;  // FP8 pools: MFMA kernel, no fused append
+  if (fused && !use_mfma) return PKV_E_UNSUPPORTED;  // the append is fused into the MFMA kernels only
+  if (fp8 && !use_mfma) return PKV_E_UNSUPPORTED;    // FP8 pools: MFMA kernel
   if (fp8 && (!scale_ok(fp8->k) || !scale_ok(fp8->v))) return PKV_E_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
@@ -279,6 +279,9 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.num_parts = plan.num_parts;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? fp8->k : 1.0) * kLog2e);
   p.out_scale = fp8 ? fp8->v : 1.f;
+  // the fused FP8 append encodes x * (1 / scale), exactly as pkv_kv_append_fp8
+  p.k_inv_scale = fp8 ? 1.f / fp8->k : 1.f;
+  p.v_inv_scale = fp8 ? 1.f / fp8->v : 1.f;
 
   hipError_t e = fp8        ? pkv::launch_decode_fp8(p, dtype, stream)
                  : use_mfma ? pkv::launch_decode_mfma(p, dtype, stream)
@@ -414,6 +417,22 @@ int pkv_paged_attn_decode_fp8(const void* q, const void* k_cache, const void* v_
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{nullptr, nullptr, nullptr}, &sc,
+                     seq_order, stream);
+}
+
+int pkv_append_paged_attn_decode_fp8(const void* q, const void* k_new, const void* v_new,
+                                     const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, int32_t max_context_len, float scale,
+                                     float k_scale, float v_scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                     int32_t dtype, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                                     const int32_t* seq_order, hipStream_t stream) {
+  if (num_seqs > 0 && !slot_mapping) return PKV_E_NULL;
+  const Fp8Scales sc{k_scale, v_scale};
+  return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
+                     workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping}, &sc,
                      seq_order, stream);
 }
 

@@ -25,6 +25,27 @@ template <> __device__ __forceinline__ float hi_f32<Fp16>(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
+// 8 elements (16 bytes) of 16-bit input to 8 E4M3 codes (8 bytes): each value
+// times inv_scale in fp32, clamped to +-448 so that the conversion saturates
+// (the hardware conversion rounds to nearest even and returns NaN past the
+// range), NaN kept NaN and given the code 0x7F.
+template <typename T>
+__device__ __forceinline__ uint2 to_e4m3(uint4 w, float inv_scale) {
+  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = lo_f32<T>(ws[e]) * inv_scale, b = hi_f32<T>(ws[e]) * inv_scale;
+    const float ca = a != a ? a : fminf(fmaxf(a, -448.f), 448.f);
+    const float cb = b != b ? b : fminf(fmaxf(b, -448.f), 448.f);
+    uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xffffu;
+    if (a != a) pk = (pk & 0xff00u) | 0x7fu;
+    if (b != b) pk = (pk & 0x00ffu) | 0x7f00u;
+    out[e >> 1] |= pk << (16 * (e & 1));
+  }
+  return uint2{out[0], out[1]};
+}
+
 // Quiet-NaN bit pattern of each storage type.
 template <typename T> inline constexpr uint16_t kNanBits = 0;
 template <> inline constexpr uint16_t kNanBits<Bf16> = 0x7fc0;

@@ -18,7 +18,10 @@
 // from the 4 tokens are gathered with byte permutes first, then widened, so
 // the regrouping costs one instruction per two operand words).
 //
-// No fused append here: the FP8 append (kv_append_fp8) is a call of its own.
+// Optionally the launch also performs the step's FP8 append, as the 16-bit
+// kernel does: leading workgroups store each new token's codes (the bytes
+// kv_append_fp8 writes, from the same encoder), and the wave that reads the
+// sub-tile holding position L-1 puts the same codes into its registers from LDS.
 #include "decode_mfma_kernel.h"
 
 namespace pkv {
@@ -84,6 +87,40 @@ __device__ __forceinline__ void v_operands(const VCodes<D> (&v)[4], u32x2 (&op)[
   }
 }
 
+// Fused FP8 append, store side: the codes kv_append_fp8 writes for token i =
+// sequence i, after the checks the decode side makes (a valid length, and the
+// slot is the slot of position L_i - 1); thread per (token, kv head, 8-dim
+// run), grid-strided over the append workgroups.
+template <typename T, int D, int NT>
+__device__ __forceinline__ void append_tokens_fp8(const DecodeParams& p) {
+  constexpr int runs = D / 8;
+  uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache_w);
+  uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache_w);
+  const int64_t total = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * runs;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < total;
+       i += static_cast<int64_t>(p.append_wgs) * NT) {
+    const int c = static_cast<int>(i % runs);
+    const int64_t th = i / runs;  // sequence * Hkv + kv head
+    const int h = static_cast<int>(th % p.num_kv_heads);
+    const int t = static_cast<int>(th / p.num_kv_heads);
+    const int64_t slot = p.slot_mapping[t];
+    const int L = p.context_lens[t];
+    if (slot < 0 || L <= 0 || bad_length(L, p)) continue;
+    const int pos = L - 1;
+    const int blk = pos / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(t) * p.max_blocks_per_seq + blk];
+    const int off = pos - blk * p.block_size;
+    if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
+        slot != static_cast<int64_t>(phys) * p.block_size + off)
+      continue;
+    const size_t row = ((static_cast<size_t>(phys) * p.num_kv_heads + h) * p.block_size + off) * D + c * 8;
+    *reinterpret_cast<uint2*>(kc + row) =
+        to_e4m3<T>(*reinterpret_cast<const uint4*>(p.k_new + th * D + c * 8), p.k_inv_scale);
+    *reinterpret_cast<uint2*>(vc + row) =
+        to_e4m3<T>(*reinterpret_cast<const uint4*>(p.v_new + th * D + c * 8), p.v_inv_scale);
+  }
+}
+
 template <int D> struct Fp8Tile {
   u32x2 k[D / 32];
   VCodes<D> v[4];
@@ -97,12 +134,18 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
   const int r = lane & 15, kg = lane >> 4;
-  const WorkItem w = decode_item(p, blockIdx.x, gridDim.x);
+  if (static_cast<int>(blockIdx.x) < p.append_wgs) {
+    append_tokens_fp8<T, D, NW * kWave>(p);
+    return;
+  }
+  const WorkItem w = decode_item(p, blockIdx.x - p.append_wgs, gridDim.x - p.append_wgs);
   if (w.seq < 0) return;
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
   if (bad_len || L == 0) {
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len);
+    // an appended token needs a position: L = 0 with a slot is a caller error
+    const bool orphan = p.slot_mapping != nullptr && p.slot_mapping[w.seq] >= 0;
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan);
     return;
   }
   const int start = w.part * p.part_tokens;
@@ -124,6 +167,21 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
     }
   }
 
+  // K and V of the token appended this step (fused append), read together
+  // with the block-table window below, with the slot and the block that holds
+  // position L-1, so the check costs no round trip of its own.
+  uint4 krun = {0u, 0u, 0u, 0u}, vrun = {0u, 0u, 0u, 0u};
+  int64_t app_slot = -1;
+  int app_phys = 0;
+  if (p.slot_mapping != nullptr) {
+    const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
+    const int c = min(static_cast<int>(threadIdx.x), D / 8 - 1);
+    krun = *reinterpret_cast<const uint4*>(p.k_new + row * D + 8 * c);
+    vrun = *reinterpret_cast<const uint4*>(p.v_new + row * D + 8 * c);
+    app_slot = p.slot_mapping[w.seq];
+    app_phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + (L - 1) / p.block_size];
+  }
+
   // lane k: pool index of this wave's k-th sub-tile (16*D codes), or -1 for a
   // block id outside the pool
   int tid = 0;
@@ -136,6 +194,36 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
               : -1;
   }
   bool bad = false;
+
+  // Fused append of the token at position L-1: the workgroup whose partition
+  // holds it encodes the token into LDS, and the wave that reads that sub-tile
+  // puts the codes into its registers in place of whatever the load returned
+  // (the pool stores are the leading workgroups' job).  A slot that is not the
+  // slot of L-1 is not written and makes the sequence's output NaN (every
+  // workgroup of the sequence checks).
+  __shared__ __align__(16) uint8_t sm_new[2][D];  // the appended token's K and V codes
+  int app_w = -1, app_k = -1, app_r = 0;          // wave, step and token row that hold it
+  if (p.slot_mapping != nullptr) {
+    const int app_pos = L - 1;
+    const int blk = app_pos / p.block_size;
+    const int off = app_pos - blk * p.block_size;
+    if (app_slot >= 0) {
+      if (static_cast<unsigned>(app_phys) >= static_cast<unsigned>(p.num_blocks) ||
+          app_slot != static_cast<int64_t>(app_phys) * p.block_size + off) {
+        bad = true;
+      } else if (app_pos >= start && app_pos < end) {
+        app_r = off & 15;
+        if (threadIdx.x < D / 8) {
+          *reinterpret_cast<uint2*>(&sm_new[0][8 * threadIdx.x]) = to_e4m3<T>(krun, p.k_inv_scale);
+          *reinterpret_cast<uint2*>(&sm_new[1][8 * threadIdx.x]) = to_e4m3<T>(vrun, p.v_inv_scale);
+        }
+        const int s_tok = (app_pos - start) >> 4;
+        app_w = s_tok % NW;
+        app_k = s_tok / NW;
+      }
+    }
+    __syncthreads();
+  }
 
   // byte offsets: K token r, dims 8kg.. (+32 B per operand j); V token 4kg, dims JV*r.. (+ one row per token)
   const int koff = r * D + kg * 8;
@@ -163,6 +251,18 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
   for (int j = 0; j < JV; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int k, Fp8Tile<D>& t) {
+    if (k == app_k && wv == app_w) {
+      // token row app_r of this sub-tile is the appended token
+      if (r == app_r) {
+#pragma unroll
+        for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x2*>(&sm_new[0][kg * 8 + 32 * j]);
+      }
+      if ((app_r >> 2) == kg) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((app_r & 3) == i) t.v[i] = *reinterpret_cast<const VCodes<D>*>(&sm_new[1][r * JV]);
+      }
+    }
     u32x2 vop[JV];
     v_operands<T, D>(t.v, vop);
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -245,15 +345,27 @@ template <> struct Fp8Shape<128> { static constexpr int kDepth = 4, kMinWaves = 
 template <typename T, int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   constexpr int S = Fp8Shape<D>::kDepth, MW = Fp8Shape<D>::kMinWaves;
-  const int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
-  if (p.part_tokens > kMaxPartitionTokens || items > 0x7fffffff) return hipErrorInvalidValue;
+  int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
+  if (p.part_tokens > kMaxPartitionTokens) return hipErrorInvalidValue;
   const int nw = (p.num_parts == 1 || p.part_tokens > kFourWaveMaxTokens) ? 8 : 4;
+  DecodeParams q = p;
+  q.append_wgs = 0;
+  if (p.slot_mapping != nullptr) {
+    // leading append workgroups, as in the 16-bit launcher: at most 256, a
+    // multiple of 8 so that the decode workgroups keep their XCD placement
+    const int64_t threads = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * (D / 8);
+    int64_t wgs = (threads + nw * kWave - 1) / (nw * kWave);
+    wgs = ((wgs < 256 ? wgs : 256) + 7) / 8 * 8;
+    q.append_wgs = static_cast<int32_t>(wgs);
+    items += wgs;
+  }
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
   if (nw == 8) {
     hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, 8, S, MW>), dim3(static_cast<unsigned>(items)), dim3(8 * kWave), 0,
-                       stream, p);
+                       stream, q);
   } else {
     hipLaunchKernelGGL((decode_fp8_kernel<T, D, G, 4, S, MW>), dim3(static_cast<unsigned>(items)), dim3(4 * kWave), 0,
-                       stream, p);
+                       stream, q);
   }
   return hipGetLastError();
 }

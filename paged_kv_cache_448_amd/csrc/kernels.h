@@ -47,6 +47,9 @@ struct DecodeParams {
   uint16_t* k_cache_w;           // the same pools, writable
   uint16_t* v_cache_w;
   int32_t append_wgs;            // leading workgroups that store the appended tokens (fused append), else 0
+  // Fused append into FP8 pools: the reciprocals of the pool scales, as
+  // kv_append_fp8 multiplies by them (unused otherwise).
+  float k_inv_scale, v_inv_scale;
   // Dispatch order (optional): work slot s decodes sequence seq_order[s], a
   // permutation of [0, num_seqs); nullptr = slot s is sequence s.
   const int32_t* seq_order;

@@ -182,3 +182,25 @@ def _prefill(**kw):
 ])
 def test_prefill_rejects_bad_arguments_before_launch(kw, status):
     assert _prefill(**kw) == status
+
+
+def _fused_fp8(**kw):
+    a = dict(q=16, kn=16, vn=16, sm=16, kc=16, vc=16, bt=16, mb=4, cl=16, mcl=64, scale=0.125, ks=0.5, vs=0.25, out=16,
+             B=2, Hq=4, Hkv=2, D=64, bs=16, N=8, dt=0, ws=NULL, wsb=0, pt=0)
+    a.update(kw)
+    p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return pkv.lib().pkv_append_paged_attn_decode_fp8(
+        p(a["q"]), p(a["kn"]), p(a["vn"]), p(a["sm"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]),
+        a["mcl"], ctypes.c_float(a["scale"]), ctypes.c_float(a["ks"]), ctypes.c_float(a["vs"]), p(a["out"]), a["B"],
+        a["Hq"], a["Hkv"], a["D"], a["bs"], a["N"], a["dt"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"], None,
+        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sm=NULL), E_NULL), (dict(kn=NULL), E_NULL), (dict(vn=NULL), E_NULL), (dict(q=NULL), E_NULL),
+    (dict(kn=24), E_SHAPE), (dict(ks=0.0), E_SHAPE), (dict(vs=float("nan")), E_SHAPE), (dict(Hq=6, Hkv=4), E_SHAPE),
+    (dict(D=96), E_UNSUPPORTED), (dict(dt=3), E_UNSUPPORTED), (dict(Hq=64, Hkv=2), E_UNSUPPORTED),
+    (dict(pt=16), E_WORKSPACE), (dict(B=0, sm=NULL), OK),
+])
+def test_fused_fp8_rejects_bad_arguments_before_launch(kw, status):
+    assert _fused_fp8(**kw) == status

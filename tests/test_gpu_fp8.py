@@ -190,3 +190,90 @@ def test_fp8_rejects_bad_scales_and_dtypes():
     t = torch.zeros((1, 1), dtype=torch.int32, device="cuda")
     with pytest.raises(pkv.PkvError):
         pkv.paged_attn_decode_fp8(q, kc, kc.clone(), t, t[0].clone(), 0.125, 1.0, 1.0)
+
+
+FUSED_PARTS = {"tiny": [0, 16], "llama3.2-1b-b64": [0, 512], "fp16-d128-g8-ragged": [0, 256],
+               "bf16-g16-bs256": [0, 1024]}
+
+
+def _poisoned_fused_pools(key, slots):
+    """The context pools with the append slots set to the NaN code, so that a read of
+    a slot's old contents instead of the appended token would show."""
+    wl = _prepared(key)[0]
+    c = wl.cfg
+    kc, vc = _device_pools(key)
+    keep = slots[slots >= 0]
+    if len(keep):
+        nan = to_dev(workloads.nan_tokens(len(keep), c), c.dtype)
+        pkv.kv_append_fp8(nan, nan, torch.from_numpy(keep).cuda(), kc, vc, K_SCALE, V_SCALE)
+    return kc, vc
+
+
+@pytest.mark.parametrize("key", list(FUSED_PARTS))
+def test_fused_fp8_append_decode_equals_two_calls(key):
+    """append_paged_attn_decode_fp8 against kv_append_fp8 + paged_attn_decode_fp8:
+    pools byte-identical and outputs bit-identical; and within tolerance of the oracle
+    over the oracle's own append."""
+    wl, _, _, _, okc, ovc = _prepared(key)
+    c = wl.cfg
+    ly = wl.layers[0]
+    q, kn, vn = to_dev(ly.q, c.dtype), to_dev(ly.k_new, c.dtype), to_dev(ly.v_new, c.dtype)
+    slots = torch.from_numpy(wl.slot_mapping).cuda()
+    tables = torch.from_numpy(wl.block_tables).cuda()
+    lens = torch.from_numpy(wl.context_lens).cuda()
+    mcl = max(int(wl.context_lens.max()), 0)
+    okc, ovc = okc.copy(), ovc.copy()
+    keep = wl.slot_mapping >= 0
+    ofp8.append(ly.k_new[keep], ly.v_new[keep], c.dtype, wl.slot_mapping[keep], okc, ovc, K_SCALE, V_SCALE,
+                num_blocks=wl.num_blocks, block_size=c.block_size)
+    ref = ofp8.decode(ly.q, okc, ovc, K_SCALE, V_SCALE, wl.block_tables, wl.context_lens, c.scale, q_dtype=c.dtype,
+                      num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads, block_size=c.block_size)
+    for pt in FUSED_PARTS[key]:
+        ka, va = _device_pools(key)
+        pkv.kv_append_fp8(kn, vn, slots, ka, va, K_SCALE, V_SCALE)
+        out_a = to_bits(pkv.paged_attn_decode_fp8(q, ka, va, tables, lens, c.scale, K_SCALE, V_SCALE,
+                                                  max_context_len=mcl, partition_tokens=pt))
+        kb, vb = _poisoned_fused_pools(key, wl.slot_mapping)
+        out_b = to_bits(pkv.append_paged_attn_decode_fp8(q, kn, vn, slots, kb, vb, tables, lens, c.scale, K_SCALE,
+                                                         V_SCALE, max_context_len=mcl, partition_tokens=pt))
+        assert np.array_equal(kb.cpu().numpy(), okc) and np.array_equal(vb.cpu().numpy(), ovc), \
+            f"{key} partition {pt}: pools differ from the oracle's append"
+        assert np.array_equal(ka.cpu().numpy(), kb.cpu().numpy()) and np.array_equal(va.cpu().numpy(),
+                                                                                      vb.cpu().numpy())
+        assert np.array_equal(out_a, out_b), f"{key} partition {pt}: fused output differs from two calls"
+        r, e = assert_parity(out_b, ref, c.dtype, f"{key} fused partition {pt}")
+        print(f"{key} partition {pt}: fused == two calls, max|err| {e:.2e}", flush=True)
+
+
+def test_fused_fp8_wrong_and_missing_slots():
+    """A slot that is not the slot of L-1 writes nothing and gives NaN in that
+    sequence only; a negative slot appends nothing and decodes the pool as it is."""
+    key = "llama3.2-1b-b64"
+    wl = _prepared(key)[0]
+    c = wl.cfg
+    ly = wl.layers[0]
+    q, kn, vn = to_dev(ly.q, c.dtype), to_dev(ly.k_new, c.dtype), to_dev(ly.v_new, c.dtype)
+    tables = torch.from_numpy(wl.block_tables).cuda()
+    lens = torch.from_numpy(wl.context_lens).cuda()
+    mcl = int(wl.context_lens.max())
+    slots = wl.slot_mapping.copy()
+    # a sequence whose position L-2 shares the block of L-1: its slot is slot - 1,
+    # inside its own context and no other sequence's append slot
+    i = next(j for j in range(len(slots)) if (int(wl.context_lens[j]) - 1) % c.block_size != 0 and j != 7)
+    wrong = int(slots[i] - 1)
+    slots[i] = wrong
+    slots[7] = -1
+    kb, vb = _device_pools(key)
+    before_k = kb.cpu().numpy().copy()
+    out = to_bits(pkv.append_paged_attn_decode_fp8(q, kn, vn, torch.from_numpy(slots).cuda(), kb, vb, tables, lens,
+                                                   c.scale, K_SCALE, V_SCALE, max_context_len=mcl))
+    got = bits_to_f64(out, c.dtype)
+    assert np.all(np.isnan(got[i])), "a wrong slot must make its sequence NaN"
+    assert np.all(np.isfinite(np.delete(got, i, axis=0)))
+    N, Hkv, bs, D = kb.shape
+    after = kb.cpu().numpy().transpose(0, 2, 1, 3).reshape(N * bs, Hkv, D)
+    assert np.array_equal(after[wrong], before_k.transpose(0, 2, 1, 3).reshape(N * bs, Hkv, D)[wrong])
+    # sequence 7 (no append) decodes the pool's old row at L-1: same as the plain decode
+    plain = to_bits(pkv.paged_attn_decode_fp8(q, kb, vb, tables, lens, c.scale, K_SCALE, V_SCALE,
+                                              max_context_len=mcl))
+    assert np.array_equal(out[7], plain[7])
