@@ -487,6 +487,10 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
     app = 2 * B * Hkv * D * (c.elem_bytes + 1) + 8 * B
     value = c.num_layers * (unique + app) / (ms_step * 1e-3) / 1e9
     dec_gbs = unique / (dec_us * 1e-6) / 1e9
+    # fused, a step is one launch per layer: the roofline is that launch's (as for 16-bit pools)
+    launch_us = 1e3 * ms_step / c.num_layers if fused else dec_us
+    launch_bytes = unique + app if fused else unique
+    launch_gbs = launch_bytes / (launch_us * 1e-6) / 1e9
     log(f"fp8 step {ms_step * 1e3:.1f} us; decode call {dec_us:.2f} us over {unique / 1e6:.2f} MB -> {dec_gbs:.0f} GB/s "
         f"= {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak")
     cpu = None
@@ -524,11 +528,14 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
                       "k_scale": k_scale, "v_scale": v_scale, "partition_tokens": part, "rotations": R},
            "schedule": ("host dispatch order (pkv_decode_schedule)" if order is not None else "sequence order"),
            "append": "fused into the decode kernel" if fused else "separate kv_append_fp8 kernel",
-           "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1), "decode_call_us": round(dec_us, 2),
+           "decode_tokens_per_s": round(B / (ms_step * 1e-3), 1), "decode_call_us": round(launch_us, 2),
            "decode_bytes_unique": unique,
-           "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                        "kernel": "decode_fp8_kernel (paged_attn_decode_fp8 call)"},
+           "roofline": {"bound": "hbm", "achieved": round(launch_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(launch_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "kernel": ("decode_fp8_kernel with the FP8 append fused, one launch per layer" if fused
+                                   else "decode_fp8_kernel (paged_attn_decode_fp8 call)")},
+           "launch_bytes": launch_bytes, "decode_only_call_us": round(dec_us, 2),
+           "decode_only_hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
            "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
 
@@ -576,13 +583,18 @@ def main():
     import workloads
     if args.pmc_summary:
         wl = workloads.build(args.config, poison=False)
+        B, c = len(wl.context_lens), wl.cfg
         if args.kv == "fp8":
-            pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name + "-fp8", fp8_decode_bytes(wl),
+            # the counter runs time the fused step: its launch also reads the appended
+            # tokens' 16-bit K/V and writes their codes
+            app8 = 2 * B * c.num_kv_heads * c.head_dim * (c.elem_bytes + 1) + 8 * B
+            pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name + "-fp8", fp8_decode_bytes(wl) + app8,
                         f"bench.py --kv fp8 --config {args.config} --steps {args.steps} --warmup {args.warmup} "
                         f"--cpu-budget 0 --copy-calibration", kernels=("decode_fp8_kernel",))
             return
         _, unique = algorithmic_bytes(wl.cfg, wl.context_lens, wl.block_tables, wl.cfg.block_size)
-        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name, unique,
+        # the counter runs time the fused launch (decode + the appended tokens' K/V)
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1], wl.cfg.name, unique + append_bytes(c, B),
                     f"bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
                     f"--cpu-budget 0 --copy-calibration")
         return
