@@ -314,8 +314,10 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
         load(min(kb + i + S, last), t[i]);
       }
     }
+    // final round: pad steps leave the state unchanged and are skipped
 #pragma unroll
-    for (int i = 0; i < S; ++i) compute(kb + i, t[i]);
+    for (int i = 0; i < S; ++i)
+      if (kb + i < n_w) compute(kb + i, t[i]);
   }
 
   l = add_xor32(add_xor16(l));

@@ -386,8 +386,12 @@ decode_mfma_kernel(DecodeParams p) {
         load(min(kb + i + SS, last), t[i]);
       }
     }
+    // the final round: pad steps leave the state unchanged, so they are
+    // skipped (a wave-uniform branch after the last loads, where the wait
+    // counts no longer matter)
 #pragma unroll
-    for (int i = 0; i < SS; ++i) compute(kb + i, t[i]);
+    for (int i = 0; i < SS; ++i)
+      if (kb + i < n_w) compute(kb + i, t[i]);
   };
   // A deep ring pays only when a wave has many sub-tiles: with few, its pad
   // steps (up to SS-1 per wave) cost more than the extra loads in flight gain,
