@@ -94,8 +94,11 @@ int pkv_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int
 
 /*
  * pkv_decode_workspace_bytes -- device workspace that pkv_paged_attn_decode
- * needs for these sizes (0 when the context fits one partition).  The _ex form
- * takes the same partition_tokens as pkv_paged_attn_decode_ex.
+ * needs for these sizes (0 when no context is split).  With the automatic
+ * plan the result covers every call with the same sizes and a max_context_len
+ * up to this one (the plan of a shorter bound may use more partitions), so a
+ * workspace sized once for the largest bound serves a whole decode loop.  The
+ * _ex form takes the same partition_tokens as pkv_paged_attn_decode_ex.
  */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t max_context_len);

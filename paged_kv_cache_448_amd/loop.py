@@ -64,6 +64,7 @@ class DecodeLoop:
         # prompt tokens one step may admit (default: a full batch of the longest prompts)
         self.max_prompt_tokens = max_prompt_tokens if max_prompt_tokens > 0 else lc.max_batch * lc.prompt_hi
         B = lc.max_batch
+        # covers every step's plan (the batch's longest context changes every step)
         ws = decode_workspace_bytes(B, lc.num_q_heads, lc.num_kv_heads, lc.head_dim, lc.block_size, lc.max_context)
         self.workspace = torch.empty(max(ws, 256), dtype=torch.uint8, device=self.device)
         self.tables_d = torch.empty(B * self.max_blocks, dtype=torch.int32, device=self.device)

@@ -87,9 +87,9 @@ def test_workspace_and_plan():
     # the Llama-3.2-1B batch shape: 64 sequences x 8 kv heads, contexts up to 2048 -> one pass, no workspace
     assert pkv.plan_partition(64, 8, 16, 2048) == 0
     assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048) == 0
-    # the long-context shape: 16 x 8 units cannot fill 256 compute units -> 2048-token partitions
+    # the long-context shape: 16 x 8 units cannot fill 256 compute units -> 1536-token partitions
     pt = pkv.plan_partition(16, 8, 256, 8192)
-    assert pt == 2048
+    assert pt == 1536
     assert pkv.decode_workspace_bytes(16, 32, 8, 64, 256, 8192) >= 16 * 32 * 4 * (64 + 2) * 4
     # a forced split sizes the workspace for its partitions
     assert pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048, partition_tokens=512) >= 64 * 32 * 4 * (64 + 2) * 4
@@ -204,3 +204,13 @@ def _fused_fp8(**kw):
 ])
 def test_fused_fp8_rejects_bad_arguments_before_launch(kw, status):
     assert _fused_fp8(**kw) == status
+
+
+def test_workspace_query_covers_every_shorter_bound():
+    """The automatic plan may cut a shorter longest context into more partitions;
+    the workspace query at a bound covers every bound below it."""
+    for B, Hkv in ((3, 8), (7, 8), (14, 2), (16, 8), (64, 1), (256, 8)):
+        for mc in (512, 4096, 8192):
+            top = pkv.decode_workspace_bytes(B, 4 * Hkv, Hkv, 64, 16, mc)
+            for m in range(16, mc + 1, 16):
+                assert pkv.decode_workspace_bytes(B, 4 * Hkv, Hkv, 64, 16, m) <= top, (B, Hkv, mc, m)
