@@ -175,7 +175,7 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
   int app_phys = 0;
   if (p.slot_mapping != nullptr) {
     const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
-    const int c = min(static_cast<int>(threadIdx.x), D / 8 - 1);
+    const int c = min(lane, D / 8 - 1);
     krun = *reinterpret_cast<const uint4*>(p.k_new + row * D + 8 * c);
     vrun = *reinterpret_cast<const uint4*>(p.v_new + row * D + 8 * c);
     app_slot = p.slot_mapping[w.seq];
@@ -195,34 +195,33 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
   }
   bool bad = false;
 
-  // Fused append of the token at position L-1: the workgroup whose partition
-  // holds it encodes the token into LDS, and the wave that reads that sub-tile
-  // puts the codes into its registers in place of whatever the load returned
-  // (the pool stores are the leading workgroups' job).  A slot that is not the
-  // slot of L-1 is not written and makes the sequence's output NaN (every
-  // workgroup of the sequence checks).
+  // Fused append of the token at position L-1: in the workgroup whose
+  // partition holds it, the wave that reads that sub-tile encodes the token
+  // into LDS of its own (no workgroup barrier) and puts the codes into its
+  // registers in place of whatever the load returned (the pool stores are the
+  // leading workgroups' job).  The slot is checked after the sub-tile loop; a
+  // slot that is not the slot of L-1 is not written and makes the sequence's
+  // output NaN (every workgroup of the sequence checks).
   __shared__ __align__(16) uint8_t sm_new[2][D];  // the appended token's K and V codes
   int app_w = -1, app_k = -1, app_r = 0;          // wave, step and token row that hold it
-  if (p.slot_mapping != nullptr) {
+  if (p.slot_mapping != nullptr && app_slot >= 0) {
     const int app_pos = L - 1;
-    const int blk = app_pos / p.block_size;
-    const int off = app_pos - blk * p.block_size;
-    if (app_slot >= 0) {
-      if (static_cast<unsigned>(app_phys) >= static_cast<unsigned>(p.num_blocks) ||
-          app_slot != static_cast<int64_t>(app_phys) * p.block_size + off) {
-        bad = true;
-      } else if (app_pos >= start && app_pos < end) {
-        app_r = off & 15;
-        if (threadIdx.x < D / 8) {
-          *reinterpret_cast<uint2*>(&sm_new[0][8 * threadIdx.x]) = to_e4m3<T>(krun, p.k_inv_scale);
-          *reinterpret_cast<uint2*>(&sm_new[1][8 * threadIdx.x]) = to_e4m3<T>(vrun, p.v_inv_scale);
+    if (app_pos >= start && app_pos < end) {
+      app_r = app_pos & 15;  // the block size is a multiple of 16
+      const int s_tok = (app_pos - start) >> 4;
+      app_w = s_tok % NW;
+      app_k = s_tok / NW;
+      if (wv == app_w) {
+        if (lane < D / 8) {
+          *reinterpret_cast<uint2*>(&sm_new[0][8 * lane]) = to_e4m3<T>(krun, p.k_inv_scale);
+          *reinterpret_cast<uint2*>(&sm_new[1][8 * lane]) = to_e4m3<T>(vrun, p.v_inv_scale);
         }
-        const int s_tok = (app_pos - start) >> 4;
-        app_w = s_tok % NW;
-        app_k = s_tok / NW;
+        // the same wave reads the codes back in its compute step
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
-    __syncthreads();
   }
 
   // byte offsets: K token r, dims 8kg.. (+32 B per operand j); V token 4kg, dims JV*r.. (+ one row per token)
@@ -318,6 +317,14 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
 #pragma unroll
     for (int i = 0; i < S; ++i)
       if (kb + i < n_w) compute(kb + i, t[i]);
+  }
+
+  if (p.slot_mapping != nullptr && app_slot >= 0) {
+    const int app_pos = L - 1;
+    const int off = app_pos - (app_pos / p.block_size) * p.block_size;
+    if (static_cast<unsigned>(app_phys) >= static_cast<unsigned>(p.num_blocks) ||
+        app_slot != static_cast<int64_t>(app_phys) * p.block_size + off)
+      bad = true;
   }
 
   l = add_xor32(add_xor16(l));

@@ -181,7 +181,6 @@ template <typename T, int D, int G, int NW, int S, int MINW>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
 decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
-  static_assert(NW * kWave >= D, "one thread per dimension stages the appended token");
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -225,15 +224,15 @@ decode_mfma_kernel(DecodeParams p) {
   // before the block-table window so that both are in flight together.
   // The slot and the physical block of position L-1 are read here too, so the
   // check below costs no round trip of its own.
+  // Lane c < D/8 holds K dims 8c .. 8c+7, lane c < 16 the V dims of row slice c.
   u32x4 krun = {0u, 0u, 0u, 0u};
-  uint16_t vnew = 0;
+  VSlice<D> vrun{};
   int64_t app_slot = -1;
   int app_phys = 0;
   if (p.slot_mapping != nullptr) {
     const size_t row = static_cast<size_t>(w.seq) * p.num_kv_heads + w.kvh;
-    const int ti = static_cast<int>(threadIdx.x);
-    krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(ti, D / 8 - 1));
-    vnew = p.v_new[row * D + min(ti, D - 1)];
+    krun = *reinterpret_cast<const u32x4*>(p.k_new + row * D + 8 * min(lane, D / 8 - 1));
+    vrun = *reinterpret_cast<const VSlice<D>*>(p.v_new + row * D + JV * r);
     app_slot = p.slot_mapping[w.seq];
     app_phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + (L - 1) / p.block_size];
   }
@@ -254,36 +253,33 @@ decode_mfma_kernel(DecodeParams p) {
 
   // Fused append of the token decoded this step, which sits at position L-1.
   // Its K and V were read together with the block-table window, so the
-  // append adds no dependent round trip before the first sub-tile loads.  The
-  // workgroup whose partition holds L-1 stages the token in LDS, and the wave
-  // that reads that sub-tile puts it into its registers in place of whatever
-  // the load returned; the same workgroup stores the token into the pools (the
-  // same bytes kv_append writes) after its sub-tile loop, where nothing waits
-  // for the stores.  A slot that is not the slot of L-1 is not written and makes the
-  // sequence's output NaN (every workgroup of the sequence checks).
+  // append adds no dependent round trip before the first sub-tile loads.  In
+  // the workgroup whose partition holds L-1, the wave that reads that sub-tile
+  // stages the token in LDS of its own (no workgroup barrier) and puts it into
+  // its registers in place of whatever the load returned; the launch's leading
+  // append workgroups store it into the pools (append_tokens).  The slot is
+  // checked against the block the table names for L-1 after the sub-tile loop,
+  // so nothing before the first loads waits for that block id; a slot that is
+  // not the slot of L-1 is not written and makes the sequence's output NaN
+  // (every workgroup of the sequence checks).
   __shared__ __align__(16) uint16_t sm_new[2][D];  // the appended token's K and V
   int app_w = -1, app_k = -1, app_r = 0;           // wave, step and token row that hold it
-  if (p.slot_mapping != nullptr) {
+  if (p.slot_mapping != nullptr && app_slot >= 0) {
     const int app_pos = L - 1;
-    const int ti = static_cast<int>(threadIdx.x);
-    const int64_t slot = app_slot;
-    const int blk = app_pos / p.block_size;
-    const int phys = app_phys;
-    const int off = app_pos - blk * p.block_size;
-    if (slot >= 0) {
-      if (static_cast<unsigned>(phys) >= static_cast<unsigned>(p.num_blocks) ||
-          slot != static_cast<int64_t>(phys) * p.block_size + off) {
-        bad = true;
-      } else if (app_pos >= start && app_pos < end) {
-        app_r = off & 15;
-        if (ti < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * ti]) = krun;
-        if (ti < D) sm_new[1][ti] = vnew;
-        const int s_tok = (app_pos - start) >> 4;
-        app_w = s_tok % NW;
-        app_k = s_tok / NW;
+    if (app_pos >= start && app_pos < end) {
+      app_r = app_pos & 15;  // the block size is a multiple of 16
+      const int s_tok = (app_pos - start) >> 4;
+      app_w = s_tok % NW;
+      app_k = s_tok / NW;
+      if (wv == app_w) {
+        if (lane < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * lane]) = krun;
+        if (lane < 16) *reinterpret_cast<VSlice<D>*>(&sm_new[1][JV * lane]) = vrun;
+        // the same wave reads the rows back in its compute step
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
-    __syncthreads();
   }
 
   // Branch-free, so that every path issues the same loads and the compiler's
@@ -403,6 +399,14 @@ decode_mfma_kernel(DecodeParams p) {
     ring(std::integral_constant<int, S>{});
   } else if (n_w > 0) {
     ring(std::integral_constant<int, (S < 2 ? S : 2)>{});
+  }
+
+  if (p.slot_mapping != nullptr && app_slot >= 0) {
+    const int app_pos = L - 1;
+    const int off = app_pos - (app_pos / p.block_size) * p.block_size;
+    if (static_cast<unsigned>(app_phys) >= static_cast<unsigned>(p.num_blocks) ||
+        app_slot != static_cast<int64_t>(app_phys) * p.block_size + off)
+      bad = true;
   }
 
   // fold the four token rows (kg) of the denominator
