@@ -114,15 +114,20 @@ def append_bytes(cfg, num_tokens):
     return 2 * 2 * num_tokens * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes + 8 * num_tokens
 
 
+def _blas_threads():
+    """Threads the oracle's numpy BLAS runs with (its matrix products are its only parallel part)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        return 1
+
+
 def cpu_baseline(wl, budget_s=10.0):
     """The oracle, as it stands, timed on this host over whole passes of the
     workload's first layer until about budget_s seconds have been spent."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # noqa: BLE001
-        blas = 1
+    blas = _blas_threads()
     c, ly = wl.cfg, wl.layers[0]
     kc, vc = ly.k_cache.copy(), ly.v_cache.copy()
     oracle.kv_append(ly.k_new, ly.v_new, wl.slot_mapping, kc, vc, num_blocks=wl.num_blocks, block_size=c.block_size)
@@ -353,7 +358,7 @@ def prefill_bench(config, steps, warmup, cpu_budget):
             if time.perf_counter() - t0 >= cpu_budget:
                 break
         dt = time.perf_counter() - t0
-        cpu = {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(done_flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _blas_threads(), "kind": "oracle",
                "sample": f"oracle.prefill over {len(used)} whole prompts of the batch ({sum(used)} tokens, "
                          f"the shortest first), {dt:.1f} s"}
     rec = {"metric": "paged prefill attention TFLOP/s (% of MI355X dense MFMA peak)", "value": round(tfs, 2),
@@ -513,7 +518,7 @@ def fp8_bench(config, steps, warmup, cpu_budget, copy_calibration=False, k_scale
             if time.perf_counter() - t0 >= cpu_budget:
                 break
         dt = (time.perf_counter() - t0) / runs
-        cpu = {"value": round(unique / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(unique / dt / 1e9, 4), "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
                "sample": f"oracle.fp8.decode over the whole first layer ({B} sequences), {runs} passes, "
                          f"{dt:.3f} s per pass", "tokens_per_s": round(B / dt, 2)}
     traffic = load_traffic(c.name + "-fp8")
