@@ -74,6 +74,12 @@ const char* pkv_status_str(int status);
 /*
  * pkv_kv_append -- store the K and V of num_tokens new tokens.
  *
+ * Each generated token's K and V are kept for every later step, in the block
+ * and offset its slot names ("vLLM -- PagedAttention으로 LLM 추론 성능을 2~4배
+ * 끌어올린 서빙 엔진", sections "KV Cache가 왜 병목인가" (K and V kept per layer
+ * and head for all past tokens) and "PagedAttention -- OS 가상 메모리에서 영감"
+ * (tokens go into fixed-size blocks taken as they arrive)).
+ *
  *   k, v          [num_tokens][num_kv_heads][head_dim]
  *   slot_mapping  [num_tokens] int64: slot of each token; a negative slot means
  *                 "padding token, write nothing"; a slot >= num_blocks*block_size
@@ -108,6 +114,16 @@ size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int3
 
 /*
  * pkv_paged_attn_decode -- out = softmax(scale * q K^T) V for each sequence.
+ *
+ * Decode: the one new token of each sequence attends to every cached token of
+ * its context, read from the KV cache rather than recomputed ("vLLM --
+ * PagedAttention으로 LLM 추론 성능을 2~4배 끌어올린 서빙 엔진", section "Prefill vs
+ * Decode"); the context is found block by block through the sequence's block
+ * table (same page, section "PagedAttention -- OS 가상 메모리에서 영감"); the
+ * formula, the causal mask (for the last position: every cached token) and GQA
+ * head sharing are those of "[Hacker News 요약] C++와 CUDA로 vLLM의 경량 고성능
+ * LLM 추론 엔진 'Tiny-vLLM' 직접 구축하기", section "고성능 추론을 위한 고급 최적화
+ * 기법".
  *
  *   q             [num_seqs][num_q_heads][head_dim]: the query of the token
  *                 being decoded.  q head h reads kv head h / G, G = Hq / Hkv.

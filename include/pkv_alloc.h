@@ -55,6 +55,22 @@ int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq_id, int32_t num_tokens);
 int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, int64_t src_seq,
                              int32_t num_shared_blocks);
 
+/* Make the first num_full_blocks logical blocks of the live sequence dst_seq
+ * the same physical blocks as src_seq's (reference counted); dst_seq's own
+ * blocks at those indices are released (returned to the pool when nobody else
+ * holds them).  Used when the caller knows that dst_seq's leading tokens equal
+ * src_seq's, so their K/V need to live in the pool once ("Nano-vLLM로 배우는
+ * vLLM 추론 엔진 작동 원리 한눈에 정리", section "KV 캐시와 Block Manager":
+ * sequences with the same prompt prefix reuse its blocks).  The shared blocks
+ * must be full in both sequences and lie before both sequences' next write:
+ * num_full_blocks * block_size <= min(len(src_seq), len(dst_seq)), so no later
+ * append writes into a shared block.  dst_seq keeps its length and its blocks
+ * past num_full_blocks.  num_full_blocks = 0 changes nothing.  PKV_E_NULL,
+ * PKV_E_NOSEQ (either sequence missing), PKV_E_SHAPE (negative count, dst_seq
+ * == src_seq, or blocks not full before the next write); on error nothing
+ * changes. */
+int pkv_alloc_share_prefix(pkv_alloc* a, int64_t dst_seq, int64_t src_seq, int32_t num_full_blocks);
+
 /* Register seq_id with a num_tokens-token prompt given by its token ids, and
  * share the longest run of leading full blocks that a live sequence already
  * holds for the same tokens (prefix caching, "Nano-vLLM로 배우는 vLLM 추론 엔진

@@ -42,6 +42,7 @@ PROTOTYPES = {
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_add_seq": (_c.c_int, [_vp, _i64, _i32]),
     "pkv_alloc_add_seq_shared": (_c.c_int, [_vp, _i64, _i32, _i64, _i32]),
+    "pkv_alloc_share_prefix": (_c.c_int, [_vp, _i64, _i64, _i32]),
     "pkv_alloc_add_seq_prefix": (_c.c_int, [_vp, _i64, _vp, _i32, _vp]),
     "pkv_alloc_append_slot": (_c.c_int, [_vp, _i64, _vp]),
     "pkv_alloc_append_slots": (_c.c_int, [_vp, _vp, _i32, _vp]),

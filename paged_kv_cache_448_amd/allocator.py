@@ -38,6 +38,11 @@ class BlockAllocator:
         check(lib().pkv_alloc_add_seq_shared(self._h, int(seq_id), int(num_tokens), int(src_seq),
                                              int(num_shared_blocks)))
 
+    def share_prefix(self, dst_seq: int, src_seq: int, num_full_blocks: int):
+        """Make dst_seq's first num_full_blocks blocks src_seq's (both live; the blocks full and
+        before both sequences' next write); dst_seq's own blocks there are released."""
+        check(lib().pkv_alloc_share_prefix(self._h, int(dst_seq), int(src_seq), int(num_full_blocks)))
+
     def add_seq_prefix(self, seq_id: int, token_ids) -> int:
         """Register seq_id with its prompt's token ids, sharing the leading full blocks a live
         sequence already holds for the same tokens; returns how many leading tokens' K/V are

@@ -162,6 +162,27 @@ int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, i
   return PKV_OK;
 }
 
+int pkv_alloc_share_prefix(pkv_alloc* a, int64_t dst_seq, int64_t src_seq, int32_t num_full_blocks) {
+  if (!a) return PKV_E_NULL;
+  auto d = a->seqs.find(dst_seq);
+  auto s = a->seqs.find(src_seq);
+  if (d == a->seqs.end() || s == a->seqs.end()) return PKV_E_NOSEQ;
+  if (num_full_blocks < 0 || dst_seq == src_seq) return PKV_E_SHAPE;
+  const int64_t tokens = static_cast<int64_t>(num_full_blocks) * a->block_size;
+  if (tokens > s->second.len || tokens > d->second.len) return PKV_E_SHAPE;
+  // take the new references before dropping the old ones, so a block that
+  // dst_seq already shares with src_seq never reaches a zero count
+  for (int32_t j = 0; j < num_full_blocks; ++j) {
+    const int32_t b = s->second.blocks[j];
+    const int32_t old = d->second.blocks[j];
+    if (b == old) continue;
+    ++a->refcount[b];
+    d->second.blocks[j] = b;
+    a->release(old);
+  }
+  return PKV_OK;
+}
+
 int pkv_alloc_add_seq_prefix(pkv_alloc* a, int64_t seq_id, const int32_t* token_ids, int32_t num_tokens,
                              int32_t* cached_tokens_out) {
   if (!a || !cached_tokens_out || (num_tokens > 0 && !token_ids)) return PKV_E_NULL;

@@ -2,6 +2,7 @@
 // tests/test_allocator.py.  After every operation the allocator's view (tables,
 // lengths, reference counts, free count) is checked against a shadow model.
 #include <cstdio>
+#include <algorithm>
 #include <cstdlib>
 #include <map>
 #include <random>
@@ -27,7 +28,7 @@ int main() {
   int64_t next_id = 0;
   std::vector<int32_t> table(MAXB);
   for (int step = 0; step < 20000; ++step) {
-    const int op = static_cast<int>(rng() % 10);
+    const int op = static_cast<int>(rng() % 11);
     if (op < 3) {
       const int n = static_cast<int>(rng() % 300);
       const int rc = pkv_alloc_add_seq(a, next_id, n);
@@ -43,6 +44,16 @@ int main() {
       if (rc == PKV_OK) lens[next_id] = n;
       else CHECK(rc == PKV_E_NOMEM);
       ++next_id;
+    } else if (op < 5 && lens.size() >= 2) {
+      // share a prefix between two live sequences
+      auto d = lens.begin(), sr = lens.begin();
+      std::advance(d, rng() % lens.size());
+      std::advance(sr, rng() % lens.size());
+      const int most = std::min(d->second, sr->second) / BS;
+      const int n = static_cast<int>(rng() % (most + 2));  // sometimes one too many
+      const int rc = pkv_alloc_share_prefix(a, d->first, sr->first, n);
+      if (d->first == sr->first || n > most) CHECK(rc == PKV_E_SHAPE);
+      else CHECK(rc == PKV_OK);
     } else if (op < 8 && !lens.empty()) {
       std::vector<int64_t> ids;
       for (auto& kv : lens)

@@ -130,3 +130,87 @@ def test_allocator_under_address_and_ub_sanitizers(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+def _state(a, ids, max_blocks=64):
+    t, L = _tables(a, ids, max_blocks)
+    return t.copy(), L.copy(), a.num_free, [a.refcount(b) for b in range(a.num_blocks)]
+
+
+def test_share_prefix_into_live_sequence():
+    a = pkv.BlockAllocator(64, 16, shuffle_seed=21)
+    a.add_seq(0, 100)                      # 7 blocks, 6 full
+    a.add_seq(1, 70)                       # 5 blocks, 4 full
+    free0 = a.num_free
+    t0, _ = _tables(a, [0, 1])
+    own = [int(b) for b in t0[1, :3]]
+    a.share_prefix(1, 0, 3)
+    t, L = _tables(a, [0, 1])
+    assert list(L) == [100, 70]
+    assert t[1, :3].tolist() == t[0, :3].tolist()          # the shared blocks
+    assert t[1, 3:5].tolist() == t0[1, 3:5].tolist()        # dst keeps its own blocks past them
+    assert a.num_free == free0 + 3                          # dst's replaced blocks went back
+    assert all(a.refcount(b) == 0 for b in own)
+    assert all(a.refcount(int(b)) == 2 for b in t[0, :3])
+    alloc_check.check_tables(t, L, num_blocks=64, block_size=16, pad_value=-1, shared=t[0, :3], appended=False)
+    # appends of both land outside the shared blocks
+    s = a.append_slots([0, 1])
+    assert not np.isin(s // 16, t[0, :3]).any()
+    t, L = _tables(a, [0, 1])
+    alloc_check.check_tables(t, L, num_blocks=64, block_size=16, pad_value=-1, shared=t[0, :3])
+    # freeing the source keeps the shared blocks alive for dst
+    a.free_seq(0)
+    assert all(a.refcount(int(b)) == 1 for b in t[1, :3])
+    a.free_seq(1)
+    assert a.num_free == 64 and all(a.refcount(b) == 0 for b in range(64))
+
+
+def test_share_prefix_chain_and_idempotence():
+    a = pkv.BlockAllocator(40, 16, shuffle_seed=2)
+    for i in range(3):
+        a.add_seq(i, 64)                   # 4 full blocks each
+    a.share_prefix(1, 0, 2)
+    a.share_prefix(2, 1, 4)                # 2 of src's blocks are 0's, 2 are 1's own
+    before = _state(a, [0, 1, 2])
+    a.share_prefix(2, 1, 4)                # already shared: nothing changes
+    a.share_prefix(2, 0, 0)                # zero blocks: nothing changes
+    after = _state(a, [0, 1, 2])
+    assert all(np.array_equal(x, y) for x, y in zip(before[:2], after[:2])) and before[2:] == after[2:]
+    t, L = _tables(a, [0, 1, 2])
+    assert t[2, :4].tolist() == t[1, :4].tolist() and t[1, :2].tolist() == t[0, :2].tolist()
+    assert [a.refcount(int(b)) for b in t[2, :4]] == [3, 3, 2, 2]
+    assert a.num_free == 40 - 4 - 2 - 0
+    alloc_check.check_tables(t, L, num_blocks=40, block_size=16, pad_value=-1, shared=t[1, :4], appended=False)
+    for i in range(3):
+        a.free_seq(i)
+    assert a.num_free == 40
+
+
+@pytest.mark.parametrize("dst,src,n,status", [
+    (1, 9, 1, NOSEQ), (9, 0, 1, NOSEQ), (1, 1, 1, SHAPE), (1, 0, -1, SHAPE),
+    (1, 0, 3, SHAPE),      # dst (40 tokens) has only 2 full blocks before its next write
+    (0, 2, 2, SHAPE),      # src (20 tokens) has only 1 full block
+])
+def test_share_prefix_errors_leave_state_unchanged(dst, src, n, status):
+    a = pkv.BlockAllocator(32, 16, shuffle_seed=4)
+    a.add_seq(0, 100)
+    a.add_seq(1, 40)
+    a.add_seq(2, 20)
+    before = _state(a, [0, 1, 2])
+    with pytest.raises(pkv.PkvError) as e:
+        a.share_prefix(dst, src, n)
+    assert e.value.status == status
+    after = _state(a, [0, 1, 2])
+    assert all(np.array_equal(x, y) for x, y in zip(before[:2], after[:2])) and before[2:] == after[2:]
+
+
+def test_share_prefix_exactly_full_boundary():
+    # 32 tokens = 2 full blocks; the next write (position 32) is in block 2
+    a = pkv.BlockAllocator(16, 16)
+    a.add_seq(0, 32)
+    a.add_seq(1, 32)
+    a.share_prefix(1, 0, 2)
+    t, L = _tables(a, [0, 1])
+    alloc_check.check_tables(t, L, num_blocks=16, block_size=16, pad_value=-1, shared=t[0, :2], appended=False)
+    s = a.append_slots([0, 1])
+    assert len(set((s // 16).tolist())) == 2 and not np.isin(s // 16, t[0, :2]).any()
