@@ -161,6 +161,30 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_paged_attn_decode_noalloc -- pkv_paged_attn_decode with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).  The
+ * split-context partial states live in a library-owned device array of 16 MiB
+ * per GPU (allocated when the library's code is loaded on that GPU, held until
+ * the process ends); the call itself allocates and frees nothing.  Results
+ * are bit-identical to pkv_paged_attn_decode with the automatic plan.
+ *
+ *   arguments as pkv_paged_attn_decode, without workspace / workspace_bytes.
+ *
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on
+ * one GPU (concurrent streams, or host threads) race and give undefined
+ * results: serialise them (one stream, or events).  Nothing in the array needs
+ * to start at zero.  PKV_E_WORKSPACE when the plan's partial states
+ * (num_seqs * num_q_heads * partitions * (head_dim + 2) * 4 bytes, rounded up)
+ * exceed 16 MiB.  Other errors as pkv_paged_attn_decode.
+ */
+int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t dtype, hipStream_t stream);
+
+/*
  * pkv_paged_attn_decode_ex -- as above, with two tuning knobs:
  *   partition_tokens  0 = automatic; otherwise a multiple of 16: the context of
  *                     each sequence is cut into partitions of this many tokens,

@@ -182,6 +182,33 @@ def paged_attn_decode(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     return out
 
 
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, *, max_context_len=None):
+    """paged_attn_decode through the allocation-free entry point: no workspace, the
+    split-context partial states in the library's per-GPU device array (calls that
+    overlap on one GPU race).  ``out`` ([B, Hq, D], q's dtype) is required, so that
+    nothing is allocated here either."""
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(q, "q", k_cache.dtype, 3)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    _device_tensor(k_cache, "k_cache")
+    _device_tensor(v_cache, "v_cache")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    _device_tensor(out, "out", q.dtype, 3)
+    _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    check(lib().pkv_paged_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M, _ptr(context_lens), int(max_context_len),
+        ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N, _dtype_code(q), _stream(q)))
+    return out
+
+
 def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale,
                              out=None, *, max_context_len=None, workspace=None, partition_tokens=0, seq_order=None):
     """kv_append of one token per sequence, then paged_attn_decode, in one launch.

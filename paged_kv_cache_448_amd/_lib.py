@@ -20,6 +20,8 @@ PROTOTYPES = {
     "pkv_decode_workspace_bytes_ex": (_c.c_size_t, [_i32] * 7),
     "pkv_paged_attn_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32, _i32,
                                          _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _vp]),
+    "pkv_paged_attn_decode_noalloc": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32,
+                                                 _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_attn_decode_ex": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp, _i32, _i32,
                                             _i32, _i32, _i32, _i32, _i32, _vp, _c.c_size_t, _i32, _i32, _vp, _vp]),
     "pkv_append_paged_attn_decode": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp,

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["api.cpp", "alloc.cpp", "kv_append.hip", "decode_simt.hip", "decode_mfma.hip", "decode_fp8.hip", "prefill_mfma.hip", "merge.hip"]
+SOURCES = ["api.cpp", "alloc.cpp", "kv_append.hip", "decode_simt.hip", "decode_mfma.hip", "decode_fp8.hip", "prefill_mfma.hip", "merge.hip", "noalloc.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -352,6 +352,26 @@ int pkv_paged_attn_decode(const void* q, const void* k_cache, const void* v_cach
                                   nullptr, stream);
 }
 
+int pkv_paged_attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, int32_t dtype, hipStream_t stream) {
+  // the split plan's partial states need more than the scratch holds: refuse
+  // before touching the device
+  if (num_seqs > 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_context_len > 0 &&
+      num_q_heads % num_kv_heads == 0) {
+    const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, 0);
+    if (workspace_for(num_seqs, num_q_heads, head_dim, plan) > pkv::kNoAllocScratchBytes) return PKV_E_WORKSPACE;
+  }
+  void* ws = nullptr;
+  if (pkv::noalloc_scratch(&ws) != hipSuccess) return PKV_E_HIP;
+  return pkv_paged_attn_decode_ex(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                  max_context_len, scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                  block_size, num_blocks, dtype, ws, pkv::kNoAllocScratchBytes, 0, PKV_IMPL_AUTO,
+                                  nullptr, stream);
+}
+
 int pkv_paged_prefill(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
                       int32_t num_tokens, int32_t max_query_len, int32_t max_context_len, float scale, void* out,

@@ -100,4 +100,11 @@ hipError_t launch_prefill_mfma(const PrefillParams& p, int dtype, hipStream_t st
 
 hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream);
 
+// Size of the device scratch of the allocation-free decode entry point
+// (split-context partial states): 16 MiB per GPU.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+// That scratch's device address on the current device (looked up once per
+// device); hipError on failure.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace pkv

@@ -214,3 +214,12 @@ def test_workspace_query_covers_every_shorter_bound():
             top = pkv.decode_workspace_bytes(B, 4 * Hkv, Hkv, 64, 16, mc)
             for m in range(16, mc + 1, 16):
                 assert pkv.decode_workspace_bytes(B, 4 * Hkv, Hkv, 64, 16, m) <= top, (B, Hkv, mc, m)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch_before_touching_the_device():
+    # 4096 sequences up to 8192 tokens, 32 q / 8 kv heads of 128 dims: the split
+    # plan's partial states need far more than the 16 MiB device scratch
+    p = ctypes.c_void_p(256)
+    st = pkv.lib().pkv_paged_attn_decode_noalloc(p, p, p, p, 32, p, 8192, ctypes.c_float(0.1), p, 4096, 32, 8, 128,
+                                                 256, 1 << 16, 0, None)
+    assert st == E_WORKSPACE
