@@ -150,6 +150,27 @@ def test_ragged_lengths_and_shapes(Hq, Hkv, D, bs, dtype):
             assert_parity(to_bits(out), ref, dtype, f"impl {impl} partition {pt}")
 
 
+# lengths around the edges of 512- and 1024-token blocks: one block, a block
+# plus one sub-tile, several blocks with a ragged tail
+BIG_BLOCK_LENS = [1, 17, 511, 512, 513, 1023, 1024, 1025, 1040, 2047, 2048, 2049, 3000, 4100]
+
+
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype", [(8, 2, 64, 512, "bf16"), (16, 2, 128, 1024, "fp16"),
+                                               (32, 8, 64, 1024, "bf16"), (4, 4, 128, 512, "fp16")])
+def test_large_block_sizes(Hq, Hkv, D, bs, dtype):
+    """Block sizes 512 and 1024 (the largest the library takes): 32 or 64 sub-tiles
+    per block and kv head, contexts across block and sub-tile edges."""
+    wl, kc, vc, dw, d = _custom(Hq, Hkv, D, bs, BIG_BLOCK_LENS, dtype, seed=bs + D + Hq)
+    ref = oracle_decode(wl, 0, kc, vc)
+    impls = [i for i in ("simt", "mfma") if pkv.decode_supported(i, dtype, D, Hq // Hkv)]
+    assert impls
+    for impl in impls:
+        for pt in (0, 16, 512, 1024, 8192):
+            out = gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt)
+            r, e = assert_parity(to_bits(out), ref, dtype, f"bs {bs} impl {impl} partition {pt}")
+            print(f"bs {bs} G {Hq // Hkv} D {D} impl {impl} partition {pt}: max|err| {e:.2e}", flush=True)
+
+
 def test_length_one_is_exactly_v0():
     lens = [1] * 9
     wl, kc, vc, dw, d = _custom(8, 2, 64, 16, lens, seed=3)

@@ -113,9 +113,12 @@ _WORKLOADS = {
                                                     seed=4),
     "fp16-d128-mha": lambda: workloads.custom(8, 8, 128, 32, [40, 1000, 257], "fp16", seed=5),
     "bf16-g16-bs256": lambda: workloads.custom(16, 1, 64, 256, [5000, 31, 2600], "bf16", seed=6),
+    "bf16-bs512": lambda: workloads.custom(8, 2, 64, 512, [1, 511, 513, 1025, 2049], "bf16", seed=7),
+    "fp16-d128-bs1024": lambda: workloads.custom(16, 2, 128, 1024, [17, 1023, 1025, 3000], "fp16", seed=8),
 }
 PARTS = {"tiny": [0, 16, 32], "llama3.2-1b-b64": [0, 4096, 128, 512], "fp16-d128-g8-ragged": [0, 2112, 256, 512],
-         "fp16-d128-mha": [0, 128], "bf16-g16-bs256": [0, 8192, 256, 1024]}
+         "fp16-d128-mha": [0, 128], "bf16-g16-bs256": [0, 8192, 256, 1024], "bf16-bs512": [0, 512, 1024],
+         "fp16-d128-bs1024": [0, 1024, 256]}
 
 
 def _device_pools(key):
@@ -193,7 +196,7 @@ def test_fp8_rejects_bad_scales_and_dtypes():
 
 
 FUSED_PARTS = {"tiny": [0, 16], "llama3.2-1b-b64": [0, 512], "fp16-d128-g8-ragged": [0, 256],
-               "bf16-g16-bs256": [0, 1024]}
+               "bf16-g16-bs256": [0, 1024], "bf16-bs512": [0, 512], "fp16-d128-bs1024": [0, 1024]}
 
 
 def _poisoned_fused_pools(key, slots):

@@ -83,6 +83,27 @@ def _custom(lens, Hq=8, Hkv=2, D=64, bs=16, dtype="bf16", seed=11):
     return wl
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype", [(8, 2, 64, 512, "bf16"), (16, 2, 128, 1024, "fp16")])
+def test_fused_large_block_sizes(Hq, Hkv, D, bs, dtype):
+    """Fused == two calls, and within tolerance of the oracle, at block sizes 512 and
+    1024; lengths across block edges, so the appended token lands at many offsets."""
+    lens = [1, 512, 513, 1024, 1025, 2047, 2049, 3000]
+    wl = _custom(lens, Hq=Hq, Hkv=Hkv, D=D, bs=bs, dtype=dtype, seed=bs)
+    kc_ref, vc_ref = oracle_caches(wl, 0)
+    ref = oracle_decode(wl, 0, kc_ref, vc_ref)
+    for pt in (0, 512):
+        dwa, da = _fresh(wl, 0)
+        out_a = to_bits(_two_calls(wl, dwa, da, pt))
+        dwb, db = _fresh(wl, 0)
+        _poison_slots(wl, dwb, db, dwb.slots)
+        out_b = to_bits(_fused(wl, dwb, db, pt))
+        assert np.array_equal(to_bits(db.k_cache).ravel(), kc_ref) and np.array_equal(to_bits(db.v_cache).ravel(),
+                                                                                         vc_ref), f"bs {bs}: pools"
+        assert np.array_equal(out_a, out_b), f"bs {bs} partition {pt}: output differs from two calls"
+        r, e = assert_parity(out_b, ref, dtype, f"bs {bs} partition {pt}")
+        print(f"bs {bs} partition {pt}: fused == two calls, max|err| {e:.2e}", flush=True)
+
+
 def test_fused_length_one_is_exactly_v_new():
     """With L = 1 the appended token is the whole context: out = v_new exactly."""
     wl = _custom([1] * 7, Hq=8, Hkv=2)

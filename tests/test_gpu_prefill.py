@@ -77,6 +77,8 @@ CASES = {
     "bf16-d128-mha": (8, 8, 128, 32, [300, 77], [300, 77], "bf16"),
     "bf16-g16-bs256": (16, 1, 64, 256, [600, 5], [250, 5], "bf16"),
     "fp16-g2-empty-seq": (4, 2, 64, 16, [40, 50, 60], [10, 0, 60], "fp16"),
+    "bf16-bs512": (8, 2, 64, 512, [1100, 513, 40], [600, 513, 1], "bf16"),
+    "fp16-d128-bs1024": (16, 2, 128, 1024, [2100, 1025], [1100, 17], "fp16"),
 }
 
 
