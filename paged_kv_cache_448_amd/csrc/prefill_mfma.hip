@@ -24,7 +24,10 @@
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
 // as in decode; the running reference is moved only when a score exceeds it by
 // more than a fixed slack, so most sub-tiles need no rescaling of the
-// accumulators (the result is the same: softmax does not depend on the shift).  A key is visible to a column when it is not after the
+// accumulators (the result is the same: softmax does not depend on the
+// shift); each lane tests its own four scores against it and the column
+// maxima are folded across lanes only when a test fires.  A key is visible
+// to a column when it is not after the
 // column's position; sub-tiles entirely before the wave's first position need
 // no mask.  Every wave sees every key its columns need, so nothing is combined
 // across waves: each lane divides and stores its columns' outputs itself.
@@ -44,16 +47,19 @@ namespace {
 // to 2^8 before the reference catches up; exact in bf16 and fp16).
 constexpr float kRescaleSlack = 8.f;
 
-// Column groups per wave: four at head_dim 64, two at 128 (accumulators of
-// 64 VGPRs either way).
+// Column groups per wave (accumulators of 64 VGPRs at either head_dim), key
+// sub-tiles in flight per wave, and workgroups per CU.  Two workgroups of
+// four waves give each wave 256 registers; at head_dim 128 a second sub-tile
+// in flight does not fit them and would spill, so that kernel loads one
+// sub-tile ahead only.
 template <int D> struct PrefillShape;
-template <> struct PrefillShape<64> { static constexpr int kGroups = 4, kDepth = 2; };
-template <> struct PrefillShape<128> { static constexpr int kGroups = 2, kDepth = 2; };
+template <> struct PrefillShape<64> { static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2; };
+template <> struct PrefillShape<128> { static constexpr int kGroups = 2, kDepth = 1, kBlocksPerCu = 2; };
 
 constexpr int kPrefillWaves = 4;
 
 template <typename T, int D, int G, int NW, int CG, int S>
-__global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillParams p) {
+__global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -185,13 +191,14 @@ __global__ __launch_bounds__(NW * kWave, 2) void prefill_mfma_kernel(PrefillPara
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = key0 + 4 * kg + i <= pos[cg] ? x[i] : -INFINITY;
       }
-      // the column's maximum, raw, then in log2 units (the scale is positive)
-      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      bm = max_xor32(max_xor16(bm)) * p.scale_log2;
       // lazy rescaling: the reference m moves only when a score exceeds it by
-      // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack
-      const bool up = bm > m[cg] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(up)) {
+      // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack;
+      // each lane checks its own scores, the column maxima are folded across
+      // lanes only when one exceeds
+      const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(lm * p.scale_log2 > m[cg] + kRescaleSlack)) {
+        const float bm = max_xor32(max_xor16(lm)) * p.scale_log2;
+        const bool up = bm > m[cg] + kRescaleSlack;
         const float mn = up ? bm : m[cg];
         const float al = fast_exp2(m[cg] - mn);
         m[cg] = mn;
