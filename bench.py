@@ -110,6 +110,14 @@ def algorithmic_bytes(cfg, lens, tables, block_size):
     return logical, unique
 
 
+def per_layer_read(wl, plan, cfg):
+    """Pool bytes the prefix decode reads per layer: each prefix item's shared
+    blocks once, every sequence's own positions after its prefix."""
+    per_tok = 2 * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes
+    return per_tok * (sum(int(plan.prefix_len[it[0]]) for it in plan.items) +
+                      int((wl.context_lens.astype(np.int64) - plan.prefix_len).sum()))
+
+
 def append_bytes(cfg, num_tokens):
     return 2 * 2 * num_tokens * cfg.num_kv_heads * cfg.head_dim * cfg.elem_bytes + 8 * num_tokens
 
@@ -565,6 +573,9 @@ def main():
                     help="paged prefill of the workload's contexts as whole prompts (TFLOP/s)")
     ap.add_argument("--schedule", default="host", choices=["host", "none"],
                     help="host: pass the dispatch order pkv_decode_schedule makes from the lengths; none: sequence order")
+    ap.add_argument("--prefix", default="auto", choices=["auto", "off"],
+                    help="read prefix blocks shared by several sequences once per prefix item "
+                         "(auto: when the host's block tables share any; off: every sequence reads its own)")
     ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
                     help="fp8: the step over FP8 (E4M3) pools (append + paged_attn_decode_fp8, fused unless --unfused)")
     args = ap.parse_args()
@@ -640,14 +651,34 @@ def main():
     # dispatch order from the host's copy of the lengths (as the block tables)
     order = torch.from_numpy(pkv.decode_schedule(wl.context_lens)).to(dev) if args.schedule == "host" else None
     mcl = int(wl.context_lens.max())
-    ws_bytes = pkv.decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, mcl,
-                                          args.partition)
+    # shared prefixes, from the host's copy of the tables (as the dispatch order)
+    plan = None
+    if args.prefix == "auto" and args.impl != "simt" and pkv.decode_supported("mfma", c.dtype, c.head_dim, c.group):
+        plan = pkv.decode_prefix_plan(wl.block_tables, wl.context_lens, c.num_q_heads, c.num_kv_heads, c.head_dim,
+                                      c.block_size)
+        if plan.num_items == 0:
+            plan = None
+    if plan is not None:
+        pre_len = torch.from_numpy(plan.prefix_len).to(dev)
+        pre_items = torch.from_numpy(np.ascontiguousarray(plan.items)).to(dev)
+        ws_bytes = pkv.decode_prefix_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, mcl,
+                                                     plan.max_prefix_len, args.partition)
+        log(f"shared prefixes: {plan.num_items} prefix items, longest prefix {plan.max_prefix_len} tokens, "
+            f"{int(plan.prefix_len.sum())} prefix tokens read once per item")
+    else:
+        ws_bytes = pkv.decode_workspace_bytes(B, c.num_q_heads, c.num_kv_heads, c.head_dim, c.block_size, mcl,
+                                              args.partition)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     part = args.partition or pkv.plan_partition(B, c.num_kv_heads, c.block_size, mcl)
     log(f"rotations R={R} ({R * pool_bytes / 2**30:.2f} GiB of pools), partition plan {part or 'single pass'} tokens, "
         f"workspace {ws_bytes} B, impl {args.impl}")
 
     def decode(t):
+        if plan is not None:
+            pkv.paged_attn_decode_prefix(t["q"], t["kc"], t["vc"], tables, lens, c.scale, pre_len, pre_items,
+                                         plan.max_prefix_len, t["out"], max_context_len=mcl, workspace=ws,
+                                         partition_tokens=args.partition, seq_order=order)
+            return
         pkv.paged_attn_decode(t["q"], t["kc"], t["vc"], tables, lens, c.scale, t["out"], max_context_len=mcl,
                               workspace=ws, partition_tokens=args.partition, impl=args.impl, seq_order=order)
 
@@ -661,6 +692,12 @@ def main():
 
     def step(i, evs=None):
         for li, t in enumerate(layers[i % R]):
+            if fused and plan is not None:
+                pkv.paged_attn_decode_prefix(t["q"], t["kc"], t["vc"], tables, lens, c.scale, pre_len, pre_items,
+                                             plan.max_prefix_len, t["out"], k_new=t["kn"], v_new=t["vn"],
+                                             slot_mapping=slots, max_context_len=mcl, workspace=ws,
+                                             partition_tokens=args.partition, seq_order=order)
+                continue
             if fused:
                 pkv.append_paged_attn_decode(t["q"], t["kn"], t["vn"], slots, t["kc"], t["vc"], tables, lens, c.scale,
                                              t["out"], max_context_len=mcl, workspace=ws,
@@ -765,7 +802,9 @@ def main():
     value = step_bytes / (ms_step * 1e-3) / 1e9
     launch_bytes = unique + app if fused else unique  # the fused launch also moves the appended tokens
     dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
-    log(f"decode bytes {unique / 1e6:.2f} MB unique, {logical / 1e6:.2f} MB logical per layer; "
+    log(f"decode bytes {unique / 1e6:.2f} MB unique, {logical / 1e6:.2f} MB logical per layer"
+        + ("" if plan is None else f" (prefix items: the kernels read {per_layer_read(wl, plan, c) / 1e6:.2f} MB)")
+        + "; "
         f"{launch_bytes / 1e6:.2f} MB per launch -> {dec_gbs:.0f} GB/s = {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak; "
         f"step {value:.0f} GB/s")
 
@@ -779,8 +818,14 @@ def main():
                "tokens_per_s": round(B / dt, 2)}
         log(f"cpu oracle: {dt:.3f} s per pass over {B} sequences ({runs} passes)")
 
-    traffic = load_traffic(c.name) if fused else None
-    if fused:
+    traffic = load_traffic(c.name) if fused and plan is None else None
+    # bytes the kernels read from the pools: each prefix item's shared blocks
+    # once, every sequence's own positions after its prefix
+    read = per_layer_read(wl, plan, c) if plan is not None else logical
+    if plan is not None:
+        kernel_desc = ("paged_attn_decode_prefix call: partition kernel with prefix units"
+                       + (" (append fused)" if fused else "") + " + merge kernel")
+    elif fused:
         kernel_desc = ("decode_mfma_kernel with the append fused, one launch per layer" if part == 0 else
                        "append_paged_attn_decode call: partition kernel (append fused) + merge kernel")
     else:
@@ -813,6 +858,9 @@ def main():
         "decode_bytes_unique": unique,
         "launch_bytes": launch_bytes,
         "decode_bytes_logical": logical,
+        "decode_bytes_read": read,
+        "prefix": None if plan is None else {"items": plan.num_items, "max_prefix_len": plan.max_prefix_len,
+                                             "prefix_tokens": int(plan.prefix_len.sum())},
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(round(traffic)),

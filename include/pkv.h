@@ -280,6 +280,88 @@ int32_t pkv_decode_plan_partition(int32_t num_seqs, int32_t num_kv_heads, int32_
 int pkv_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t* seq_order);
 
 /*
+ * Shared prefixes read once.  Sequences that share prompt-prefix blocks by
+ * reference ("Nano-vLLM로 배우는 vLLM 추론 엔진 작동 원리 한눈에 정리", section
+ * "KV 캐시와 Block Manager": identical prefix blocks are reused instead of
+ * stored again; a block manager hands out such tables) hold the same K/V in
+ * those blocks.  The decode below reads such a prefix once for a whole
+ * prefix item of up to 16 sequences instead of once per sequence; results
+ * equal those of pkv_paged_attn_decode up to fp32 rounding order.
+ *
+ * pkv_decode_prefix_plan -- find the items from the host's copy of the block
+ * tables and context lengths (host memory only; no device call).
+ *
+ *   block_tables, max_blocks_per_seq, context_lens, num_seqs, num_q_heads,
+ *   num_kv_heads, head_dim, block_size: as the decode call takes them (the
+ *                 lengths include the token appended this step).
+ *   prefix_len    [num_seqs] int32, written: shared tokens of each sequence
+ *                 (0: none), a multiple of block_size; only blocks that are
+ *                 full before the sequence's last position are shared.
+ *   prefix_items  [max_items][16] int32, written: the members of each item
+ *                 (-1 pads), member 0 the reference whose table row the
+ *                 kernel reads; every sequence with prefix_len > 0 is in
+ *                 exactly one item, and its first prefix_len / block_size
+ *                 table entries equal the reference's.  num_seqs / 2 items
+ *                 always suffice.  Members per item: 16/G column slots per
+ *                 column group, two column groups at head_dim 64 and one at
+ *                 128 (at most G).
+ *   num_items, max_prefix_len  written: items found, longest prefix_len.
+ * Rows sharing their first block are grouped (rows sorted block by block);
+ * an item ends at the member limit or at a row that does not share its
+ * reference's first block.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (max_items too small, bad sizes),
+ * PKV_E_UNSUPPORTED (as the MFMA kernel).
+ */
+int pkv_decode_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t* prefix_len, int32_t* prefix_items, int32_t max_items,
+                           int32_t* num_items, int32_t* max_prefix_len);
+
+/*
+ * pkv_decode_prefix_workspace_bytes -- workspace of pkv_paged_attn_decode_prefix
+ * (the partition states plus one state per prefix chunk per sequence and q
+ * head); max_prefix_len 0 gives pkv_decode_workspace_bytes_ex.
+ */
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                         int32_t max_prefix_len, int32_t partition_tokens);
+
+/*
+ * pkv_paged_attn_decode_prefix -- pkv_paged_attn_decode (MFMA kernel, 16-bit
+ * pools) with shared prefixes read once per item, optionally with the step's
+ * append fused in as pkv_append_paged_attn_decode (slot_mapping NULL: no
+ * append; k_new / v_new unused then).
+ *
+ *   prefix_len, prefix_items  device copies of pkv_decode_prefix_plan's
+ *                 output (or arrays with the same properties);
+ *   num_prefix_items, max_prefix_len  its counts (host values).  Either 0:
+ *                 the plain decode (prefix_len is not read).
+ *   workspace     at least pkv_decode_prefix_workspace_bytes(...) bytes.
+ *   the other arguments as pkv_append_paged_attn_decode.
+ *
+ * Sequence i's positions 0 .. prefix_len[i]-1 are read from its item's
+ * reference row, the rest from its own.  The kernel checks each member's
+ * table against the reference row over the blocks it reads for it; a
+ * sequence whose table differs there, whose prefix_len is not a multiple of
+ * 16, not below L_i or above max_prefix_len or the reference's own, gets NaN
+ * instead.  A sequence with prefix_len > 0 that is in no item, or in two,
+ * gets an unspecified output (the item list is the caller's to keep).
+ * Positions a member masks are still multiplied by probability 0 in P.V, so
+ * cached values must be finite.
+ * Errors: as pkv_append_paged_attn_decode; PKV_E_UNSUPPORTED for shapes the
+ * MFMA kernel does not take; PKV_E_SHAPE for negative counts or
+ * max_prefix_len above max_context_len.
+ */
+int pkv_paged_attn_decode_prefix(const void* q, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                                 float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                                 const int32_t* prefix_len, const int32_t* prefix_items, int32_t num_prefix_items,
+                                 int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
+                                 int32_t partition_tokens, const int32_t* seq_order, hipStream_t stream);
+
+/*
  * pkv_decode_supported -- 1 if the decode kernel `impl` (PKV_IMPL_*) is built for
  * this dtype, head_dim and GQA group size G = Hq / Hkv, else 0.
  */

@@ -33,7 +33,8 @@ from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
 
 __all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes",
            "decode_supported", "plan_partition", "new_cache", "new_cache_fp8", "cache_dims", "kv_append_fp8",
-           "paged_attn_decode_fp8", "paged_prefill", "BlockAllocator", "PkvError", "lib"]
+           "paged_attn_decode_fp8", "paged_prefill", "decode_prefix_plan", "decode_prefix_workspace_bytes",
+           "paged_attn_decode_prefix", "PrefixPlan", "BlockAllocator", "PkvError", "lib"]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
 IMPLS = {"auto": 0, "simt": 1, "mfma": 2}
@@ -252,6 +253,102 @@ def append_paged_attn_decode(q, k_new, v_new, slot_mapping, k_cache, v_cache, bl
         _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
         _dtype_code(q), _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens),
         _order_ptr(seq_order, B), _stream(q)))
+    return out
+
+
+class PrefixPlan:
+    """Shared-prefix work found by decode_prefix_plan: ``prefix_len`` (int32 [B]),
+    ``items`` (int32 [num_items, 16], member 0 the reference, -1 pads) and
+    ``max_prefix_len``, as host numpy arrays / ints."""
+
+    def __init__(self, prefix_len, items, max_prefix_len):
+        self.prefix_len = prefix_len
+        self.items = items
+        self.max_prefix_len = int(max_prefix_len)
+
+    @property
+    def num_items(self):
+        return int(self.items.shape[0])
+
+
+def decode_prefix_plan(block_tables, context_lens, num_q_heads, num_kv_heads, head_dim, block_size):
+    """Group the sequences whose block tables start with the same blocks (host
+    numpy int32 tables [B, M] and lengths [B]) into prefix items for
+    paged_attn_decode_prefix.  Returns a PrefixPlan."""
+    tables = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    _need(tables.ndim == 2 and lens.ndim == 1 and tables.shape[0] == lens.shape[0],
+          "block_tables must be [B, M] and context_lens [B]")
+    B, M = (int(x) for x in tables.shape)
+    cap = B // 2 + 1
+    prefix_len = np.zeros(B, dtype=np.int32)
+    items = np.full((cap, 16), -1, dtype=np.int32)
+    n = ctypes.c_int32()
+    longest = ctypes.c_int32()
+    check(lib().pkv_decode_prefix_plan(tables.ctypes.data, M, lens.ctypes.data, B, int(num_q_heads),
+                                       int(num_kv_heads), int(head_dim), int(block_size), prefix_len.ctypes.data,
+                                       items.ctypes.data, cap, ctypes.byref(n), ctypes.byref(longest)))
+    return PrefixPlan(prefix_len, items[:n.value].copy(), longest.value)
+
+
+def decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, max_context_len,
+                                  max_prefix_len, partition_tokens=0):
+    return int(lib().pkv_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                                       max_context_len, max_prefix_len, partition_tokens))
+
+
+def paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens, scale, prefix_len, prefix_items,
+                             max_prefix_len, out=None, *, k_new=None, v_new=None, slot_mapping=None,
+                             max_context_len=None, workspace=None, partition_tokens=0, seq_order=None):
+    """paged_attn_decode (MFMA kernel) with shared prefixes read once per prefix item,
+    optionally with the step's append fused in (k_new, v_new, slot_mapping as in
+    append_paged_attn_decode).
+
+    prefix_len: int32 [B] and prefix_items: int32 [n, 16], device copies of a
+    PrefixPlan's arrays; max_prefix_len: its host bound.
+    """
+    N, Hkv, bs, D = cache_dims(k_cache)
+    _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
+    _device_tensor(q, "q", k_cache.dtype, 3)
+    B, Hq, Dq = (int(x) for x in q.shape)
+    _need(Dq == D, f"q head_dim {Dq} != cache head_dim {D}")
+    fused = slot_mapping is not None
+    if fused:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _device_tensor(t, name, k_cache.dtype, 3)
+            _need(tuple(t.shape) == (B, Hkv, D), f"{name} must be [{B}, {Hkv}, {D}], got {tuple(t.shape)}")
+        _device_tensor(slot_mapping, "slot_mapping", torch.int64, 1)
+        _need(slot_mapping.shape[0] == B, "slot_mapping must have one slot per sequence")
+    _device_tensor(k_cache, "k_cache")
+    _device_tensor(v_cache, "v_cache")
+    _device_tensor(block_tables, "block_tables", torch.int32, 2)
+    _need(block_tables.shape[0] == B, "block_tables must have one row per sequence")
+    _device_tensor(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens.shape[0] == B, "context_lens must have one entry per sequence")
+    _device_tensor(prefix_len, "prefix_len", torch.int32, 1)
+    _need(prefix_len.shape[0] == B, "prefix_len must have one entry per sequence")
+    _device_tensor(prefix_items, "prefix_items", torch.int32, 2)
+    _need(prefix_items.shape[1] == 16, "prefix_items must be [n, 16]")
+    M = int(block_tables.shape[1])
+    if max_context_len is None:
+        max_context_len = M * bs
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _device_tensor(out, "out", q.dtype, 3)
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+    need = decode_prefix_workspace_bytes(B, Hq, Hkv, D, bs, max_context_len, max_prefix_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    check(lib().pkv_paged_attn_decode_prefix(
+        _ptr(q), _ptr(k_new) if fused else None, _ptr(v_new) if fused else None,
+        _ptr(slot_mapping) if fused else None, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), M,
+        _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
+        _dtype_code(q), _ptr(prefix_len), _ptr(prefix_items), int(prefix_items.shape[0]), int(max_prefix_len),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _order_ptr(seq_order, B),
+        _stream(q)))
     return out
 
 

@@ -59,10 +59,49 @@ Plan make_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t max_ctx, int32_t 
   return {pt, parts};
 }
 
-size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, const Plan& plan) {
-  if (plan.num_parts <= 1) return 0;
-  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * plan.num_parts;
+// Partial-state bytes: num_parts + prefix_chunks slots per (sequence, q head),
+// none when a single pass writes every output.
+size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, const Plan& plan,
+                     int32_t prefix_chunks = 0) {
+  const int64_t slots = static_cast<int64_t>(plan.num_parts) + prefix_chunks;
+  if (slots <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * slots;
   return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
+}
+
+// Tokens of a shared prefix one prefix unit (a wave) takes: about a quarter
+// of the longest prefix, so its units spread over four times as many waves,
+// between 64 and 1024 tokens (a wave holds the ids of at most 64 sub-tiles).
+int32_t prefix_chunk_tokens(int32_t max_prefix_len) {
+  int32_t c = (max_prefix_len + 3) / 4;
+  c = (c + 15) / 16 * 16;
+  return c < 64 ? 64 : (c > 1024 ? 1024 : c);
+}
+
+int32_t prefix_chunk_count(int32_t max_prefix_len) {
+  if (max_prefix_len <= 0) return 0;
+  const int32_t c = prefix_chunk_tokens(max_prefix_len);
+  return (max_prefix_len + c - 1) / c;
+}
+
+// Auto-plan workspace bound over every longest context up to max_context_len
+// (the automatic plan is not monotone in it; plans change only at multiples of 16).
+size_t auto_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t max_context_len, int32_t prefix_chunks);
+
+// The automatic plan is not monotone in the longest context (a shorter one
+// may be cut into more, smaller partitions), so report the most any longest
+// context up to max_context_len needs: one workspace then serves every later
+// call whose bound is at most this one.
+size_t auto_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t max_context_len, int32_t prefix_chunks) {
+  size_t need = 0;
+  for (int32_t m = 16; m < max_context_len + 16; m += 16) {
+    const Plan plan = make_plan(num_seqs, num_kv_heads, m < max_context_len ? m : max_context_len, 0);
+    const size_t w = workspace_for(num_seqs, num_q_heads, head_dim, plan, prefix_chunks);
+    if (w > need) need = w;
+  }
+  return need;
 }
 
 }  // namespace
@@ -164,24 +203,22 @@ int pkv_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t* 
 size_t pkv_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t block_size, int32_t max_context_len,
                                      int32_t partition_tokens) {
+  return pkv_decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+                                           max_context_len, 0, partition_tokens);
+}
+
+size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                         int32_t max_prefix_len, int32_t partition_tokens) {
   (void)block_size;
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
     return 0;
+  const int32_t chunks = prefix_chunk_count(max_prefix_len);
   if (partition_tokens > 0) {
     const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
-    return workspace_for(num_seqs, num_q_heads, head_dim, plan);
+    return workspace_for(num_seqs, num_q_heads, head_dim, plan, chunks);
   }
-  // The automatic plan is not monotone in the longest context (a shorter one
-  // may be cut into more, smaller partitions), so report the most any longest
-  // context up to max_context_len needs: one workspace then serves every later
-  // call whose bound is at most this one.  Plans change only at multiples of 16.
-  size_t need = 0;
-  for (int32_t m = 16; m < max_context_len + 16; m += 16) {
-    const Plan plan = make_plan(num_seqs, num_kv_heads, m < max_context_len ? m : max_context_len, 0);
-    const size_t w = workspace_for(num_seqs, num_q_heads, head_dim, plan);
-    if (w > need) need = w;
-  }
-  return need;
+  return auto_workspace(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, chunks);
 }
 
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -205,6 +242,13 @@ struct Fp8Scales {
   float k, v;
 };
 
+// Shared-prefix work (nullptr: none); device arrays as pkv_paged_attn_decode_prefix takes them.
+struct PrefixDesc {
+  const int32_t* prefix_len;
+  const int32_t* prefix_items;
+  int32_t num_items, max_prefix_len;
+};
+
 bool scale_ok(float s) { return s > 0.f && s <= 3.4e38f; }  // positive and finite (NaN fails both)
 
 int decode_call(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -212,7 +256,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace, size_t workspace_bytes,
                 int32_t partition_tokens, int32_t impl, const FusedAppend& app, const Fp8Scales* fp8,
-                const int32_t* seq_order, hipStream_t stream) {
+                const int32_t* seq_order, hipStream_t stream, const PrefixDesc* pre = nullptr) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_E_SHAPE;
@@ -246,18 +290,26 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (fused && !use_mfma) return PKV_E_UNSUPPORTED;  // the append is fused into the MFMA kernels only
   if (fp8 && !use_mfma) return PKV_E_UNSUPPORTED;    // FP8 pools: MFMA kernel
   if (fp8 && (!scale_ok(fp8->k) || !scale_ok(fp8->v))) return PKV_E_SHAPE;
+  if (pre && (pre->num_items < 0 || pre->max_prefix_len < 0 || pre->max_prefix_len > max_context_len))
+    return PKV_E_SHAPE;
+  // no items or no prefix length: the call is the plain decode
+  const bool prefixed = pre && pre->num_items > 0 && pre->max_prefix_len > 0;
+  if (prefixed && (!use_mfma || fp8)) return PKV_E_UNSUPPORTED;  // shared prefixes: MFMA kernel, 16-bit pools
   if (num_seqs == 0) return PKV_OK;
+  if (prefixed && (!pre->prefix_len || !pre->prefix_items)) return PKV_E_NULL;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
   if (fused && (!app.k_new || !app.v_new)) return PKV_E_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_E_SHAPE;
   if (fused && (!aligned16(app.k_new) || !aligned16(app.v_new))) return PKV_E_SHAPE;
 
   const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
-  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, plan);
+  const int32_t chunks = prefixed ? prefix_chunk_count(pre->max_prefix_len) : 0;
+  const size_t need = workspace_for(num_seqs, num_q_heads, head_dim, plan, chunks);
   if (need > 0 && (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return PKV_E_WORKSPACE;
   const int64_t items = static_cast<int64_t>(num_seqs) * plan.num_parts * num_kv_heads;
   if (items > INT_MAX) return PKV_E_SHAPE;
+  if (prefixed && static_cast<int64_t>(pre->num_items) * num_kv_heads * chunks > INT_MAX) return PKV_E_SHAPE;
 
   pkv::DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
@@ -270,7 +322,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.part_m = nullptr;
   p.part_l = nullptr;
   if (need > 0) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * plan.num_parts;
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * (plan.num_parts + chunks);
     char* ws = static_cast<char*>(workspace);
     p.part_o = reinterpret_cast<float*>(ws);
     p.part_m = reinterpret_cast<float*>(ws + align256(rows * head_dim * sizeof(float)));
@@ -293,6 +345,14 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.max_context_len = max_context_len;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
+  p.prefix_len = prefixed ? pre->prefix_len : nullptr;
+  p.prefix_items = prefixed ? pre->prefix_items : nullptr;
+  p.num_prefix_items = prefixed ? pre->num_items : 0;
+  p.max_prefix_len = prefixed ? pre->max_prefix_len : 0;
+  p.prefix_chunk = prefixed ? prefix_chunk_tokens(pre->max_prefix_len) : 0;
+  p.prefix_chunks = chunks;
+  p.prefix_wgs = 0;  // set by the MFMA launcher
+  p.num_slots = plan.num_parts + chunks;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? fp8->k : 1.0) * kLog2e);
   p.out_scale = fp8 ? fp8->v : 1.f;
   // the fused FP8 append encodes x * (1 / scale), exactly as pkv_kv_append_fp8
@@ -303,7 +363,7 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
                  : use_mfma ? pkv::launch_decode_mfma(p, dtype, stream)
                             : pkv::launch_decode_simt(p, dtype, stream);
   if (e != hipSuccess) return PKV_E_HIP;
-  if (plan.num_parts > 1) {
+  if (plan.num_parts + chunks > 1) {
     e = pkv::launch_merge(p, dtype, stream);
     if (e != hipSuccess) return PKV_E_HIP;
   }
@@ -470,6 +530,100 @@ int pkv_append_paged_attn_decode_fp8(const void* q, const void* k_new, const voi
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping}, &sc,
                      seq_order, stream);
+}
+
+int pkv_decode_prefix_plan(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t* prefix_len, int32_t* prefix_items, int32_t max_items,
+                           int32_t* num_items, int32_t* max_prefix_len) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_items < 0)
+    return PKV_E_SHAPE;
+  if (num_q_heads % num_kv_heads) return PKV_E_SHAPE;
+  if (!block_size_ok(block_size)) return PKV_E_UNSUPPORTED;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (!pkv::mfma_supported(PKV_BF16, head_dim, group)) return PKV_E_UNSUPPORTED;
+  if (!num_items || !max_prefix_len) return PKV_E_NULL;
+  *num_items = 0;
+  *max_prefix_len = 0;
+  if (num_seqs == 0) return PKV_OK;
+  if (!block_tables || !context_lens || !prefix_len || (max_items > 0 && !prefix_items)) return PKV_E_NULL;
+  const int32_t per_item = pkv::prefix_members_per_item(head_dim, group);
+  const size_t row = static_cast<size_t>(max_blocks_per_seq);
+
+  // full[i]: sequence i's blocks that are full before its last position (the
+  // only ones it may share: the token of this step goes after them)
+  std::vector<int32_t> full(num_seqs, 0), cand;
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    prefix_len[i] = 0;
+    const int64_t L = context_lens[i];
+    if (L < 2 || L > static_cast<int64_t>(max_blocks_per_seq) * block_size) continue;
+    full[i] = static_cast<int32_t>((L - 1) / block_size);
+    if (full[i] > 0) cand.push_back(i);
+  }
+  // leading blocks two sequences have in common (within both full ranges)
+  auto common = [&](int32_t a, int32_t b) {
+    const int32_t n = std::min(full[a], full[b]);
+    const int32_t* ra = block_tables + static_cast<size_t>(a) * row;
+    const int32_t* rb = block_tables + static_cast<size_t>(b) * row;
+    int32_t k = 0;
+    while (k < n && ra[k] == rb[k]) ++k;
+    return k;
+  };
+  // rows in lexicographic order of their full blocks, a row that is a prefix
+  // of another after it (so sequences with long common prefixes are neighbours
+  // and each run starts with its longest row)
+  std::stable_sort(cand.begin(), cand.end(), [&](int32_t a, int32_t b) {
+    const int32_t k = common(a, b);
+    if (k < full[a] && k < full[b])
+      return block_tables[static_cast<size_t>(a) * row + k] < block_tables[static_cast<size_t>(b) * row + k];
+    return full[a] > full[b];
+  });
+  // items: a reference and the following rows that share at least its first
+  // block, up to per_item members; an item of one member is dropped
+  int32_t items = 0, longest = 0;
+  size_t i = 0;
+  std::vector<int32_t> mem, lim;
+  while (i < cand.size()) {
+    const int32_t ref = cand[i];
+    mem.assign(1, ref);
+    lim.assign(1, 0);
+    size_t j = i + 1;
+    for (; j < cand.size() && static_cast<int32_t>(mem.size()) < per_item; ++j) {
+      const int32_t c = common(cand[j], ref);
+      if (c < 1) break;
+      mem.push_back(cand[j]);
+      lim.push_back(c);
+    }
+    i = j;
+    if (mem.size() < 2) continue;
+    if (items >= max_items) return PKV_E_SHAPE;
+    lim[0] = *std::max_element(lim.begin() + 1, lim.end());
+    int32_t* out = prefix_items + static_cast<size_t>(items) * 16;
+    for (int32_t k = 0; k < 16; ++k) out[k] = k < static_cast<int32_t>(mem.size()) ? mem[k] : -1;
+    for (size_t k = 0; k < mem.size(); ++k) {
+      prefix_len[mem[k]] = lim[k] * block_size;
+      longest = std::max(longest, lim[k] * block_size);
+    }
+    ++items;
+  }
+  *num_items = items;
+  *max_prefix_len = longest;
+  return PKV_OK;
+}
+
+int pkv_paged_attn_decode_prefix(const void* q, const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                                 void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                                 float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
+                                 const int32_t* prefix_len, const int32_t* prefix_items, int32_t num_prefix_items,
+                                 int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
+                                 int32_t partition_tokens, const int32_t* seq_order, hipStream_t stream) {
+  const PrefixDesc pre{prefix_len, prefix_items, num_prefix_items, max_prefix_len};
+  return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                     out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
+                     workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping},
+                     nullptr, seq_order, stream, &pre);
 }
 
 }  // extern "C"

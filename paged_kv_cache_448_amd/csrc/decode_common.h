@@ -45,6 +45,20 @@ __device__ __forceinline__ bool bad_length(int L, const DecodeParams& p) {
          static_cast<int64_t>(L) > static_cast<int64_t>(p.max_blocks_per_seq) * p.block_size;
 }
 
+// The shared-prefix length pl of a sequence of length L is usable when it is
+// 0, or a positive multiple of 16 before the sequence's last position (so the
+// token appended this step is never in it) and within the launch's bound.
+__device__ __forceinline__ bool prefix_ok(int pl, int L, const DecodeParams& p) {
+  return pl == 0 || (pl > 0 && (pl & 15) == 0 && pl <= L - 1 && pl <= p.max_prefix_len);
+}
+
+// Prefix length of sequence seq (0 without prefixes); -1 when unusable.
+__device__ __forceinline__ int seq_prefix(const DecodeParams& p, int seq, int L) {
+  if (p.prefix_len == nullptr) return 0;
+  const int pl = p.prefix_len[seq];
+  return prefix_ok(pl, L, p) ? pl : -1;
+}
+
 // For an empty or invalid sequence the workgroup of partition 0 writes the
 // G heads' output (zeros or NaN); the others do nothing.
 template <typename T, int G, int NT>
@@ -81,7 +95,7 @@ __device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const 
     if (single) {
       p.out[row * D + d] = to_bits<T>(o / lt);
     } else {
-      const size_t pr = row * p.num_parts + w.part;
+      const size_t pr = row * p.num_slots + w.part;
       p.part_o[pr * D + d] = o;
       if (d == 0) {
         p.part_m[pr] = M;
@@ -92,16 +106,19 @@ __device__ __forceinline__ void combine_and_store(const float (*sm_m)[G], const 
 }
 
 // Output element (row = sequence * Hq + q head, dim d) of a split context,
-// folded from the first nparts partition states of that row in index order
-// with the log-sum-exp identity, as a running (M, l, o) so that all loads of a
-// row can be in flight together.
+// folded from the row's partial states in slot order -- the first nparts
+// partition slots, then nprefix prefix slots from slot num_parts on -- with
+// the log-sum-exp identity, as a running (M, l, o) so that all loads of a row
+// can be in flight together.
 template <int D>
-__device__ __forceinline__ float merge_row_elem(const DecodeParams& p, size_t row, int d, int nparts) {
-  const size_t base = row * p.num_parts;
+__device__ __forceinline__ float merge_row_elem(const DecodeParams& p, size_t row, int d, int nparts, int nprefix) {
+  const size_t base = row * p.num_slots;
   float M = -INFINITY, lt = 0.f, o = 0.f;
+  const int n = nparts + nprefix;
 #pragma unroll 4
-  for (int k = 0; k < nparts; ++k) {
-    const float mk = p.part_m[base + k], lk = p.part_l[base + k], ok = p.part_o[(base + k) * D + d];
+  for (int i = 0; i < n; ++i) {
+    const size_t k = base + (i < nparts ? i : p.num_parts + (i - nparts));
+    const float mk = p.part_m[k], lk = p.part_l[k], ok = p.part_o[k * D + d];
     const float mn = fmaxf(M, mk);
     const float a = fast_exp2(M - mn), b = fast_exp2(mk - mn);
     lt = fmaf(lt, a, lk * b);

@@ -36,13 +36,28 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     q.append_wgs = static_cast<int32_t>(wgs);
     items += wgs;
   }
+  q.prefix_wgs = 0;
+  if (p.prefix_len != nullptr) {
+    // shared-prefix units, one per wave, in a multiple of 8 workgroups (as the
+    // append ones) right after the append workgroups
+    const int64_t units = static_cast<int64_t>(p.num_prefix_items) * p.num_kv_heads * p.prefix_chunks;
+    const int64_t wgs = ((units + nw - 1) / nw + 7) / 8 * 8;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    q.prefix_wgs = static_cast<int32_t>(wgs);
+    items += wgs;
+  }
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  if (nw == 8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W>), dim3(static_cast<unsigned>(items)), dim3(8 * kWave),
-                       0, stream, q);
+  const dim3 grid(static_cast<unsigned>(items));
+  if (p.prefix_len != nullptr) {
+    if (nw == 8) {
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W, true>), grid, dim3(8 * kWave), 0, stream, q);
+    } else {
+      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W, true>), grid, dim3(4 * kWave), 0, stream, q);
+    }
+  } else if (nw == 8) {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W, false>), grid, dim3(8 * kWave), 0, stream, q);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W>), dim3(static_cast<unsigned>(items)), dim3(4 * kWave),
-                       0, stream, q);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W, false>), grid, dim3(4 * kWave), 0, stream, q);
   }
   return hipGetLastError();
 }

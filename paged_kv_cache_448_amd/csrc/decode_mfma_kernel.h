@@ -169,6 +169,232 @@ __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
   }
 }
 
+// Shared prefixes read once per prefix item.  Sequences whose block tables
+// start with the same physical blocks hold the same K/V there (blocks are
+// shared by reference, "Nano-vLLM로 배우는 vLLM 추론 엔진 작동 원리 한눈에 정리",
+// section "KV 캐시와 Block Manager").  A prefix item puts up to CG * 16/G of
+// them into the MFMA columns -- column (cg, r) is member cg*16/G + r/G, q
+// head kvh*G + r%G -- and one wave streams a chunk of the reference member's
+// shared blocks for all of them, each column masked at its own member's
+// prefix length.  It writes each member's softmax state over the chunk into
+// the partial-state slot num_parts + chunk; the merge folds those with the
+// states of the member's regular partitions, which start after the prefix.
+//
+// Before the first sub-tile the wave checks, block by block, that every
+// member's table names the reference's block wherever it reads that member's
+// prefix; a member that differs (or claims more prefix than the reference,
+// or whose reference is unusable) gets NaN in its state, so a wrong plan
+// shows as NaN output rather than as another sequence's attention.
+//
+// Masked keys contribute probability 0 but are multiplied into P.V, so a
+// non-finite V value in a reference block past a member's prefix length would
+// reach that member; cached values are finite.
+template <typename T, int D, int G>
+__device__ __forceinline__ void prefix_unit(const DecodeParams& p, int unit) {
+  constexpr int JK = D / 32, JV = D / 16;
+  constexpr int CG = prefix_column_groups(D, G);
+  constexpr int MPC = 16 / G;     // members per column group
+  constexpr int NM = CG * MPC;    // members per item, <= 16
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = lane & 15, kg = lane >> 4;
+  const int chunk = unit % p.prefix_chunks;
+  unit /= p.prefix_chunks;
+  const int kvh = unit % p.num_kv_heads;
+  const int item = unit / p.num_kv_heads;
+  if (item >= p.num_prefix_items) return;
+  const int32_t* mem = p.prefix_items + static_cast<size_t>(item) * 16;
+  const int c0 = chunk * p.prefix_chunk;
+
+  // the reference member and its usable prefix length (-1: unusable)
+  const int ref = mem[0];
+  int ref_lim = -1;
+  if (static_cast<unsigned>(ref) < static_cast<unsigned>(p.num_seqs)) {
+    const int Lr = p.context_lens[ref];
+    if (!bad_length(Lr, p)) ref_lim = seq_prefix(p, ref, Lr);
+  }
+
+  // lane mi < NM: member mi's sequence and prefix length; mlim = 0: no prefix
+  // part here (absent, no prefix, or an unusable length, which the regular
+  // items turn into NaN themselves); mbad: a prefix this item cannot serve
+  int ms = -1, mlim = 0;
+  bool mbad = false;
+  if (lane < NM) {
+    const int sq = mem[lane];
+    if (static_cast<unsigned>(sq) < static_cast<unsigned>(p.num_seqs)) {
+      const int L = p.context_lens[sq];
+      const int pl = bad_length(L, p) ? 0 : seq_prefix(p, sq, L);
+      if (pl > 0) {
+        ms = sq;
+        mlim = pl;
+        mbad = pl > ref_lim;
+      }
+    }
+  }
+  if (ref_lim <= c0) {
+    // nothing of the reference in this chunk: only chunk 0 reports the
+    // members this item cannot serve
+    if (chunk != 0) return;
+  }
+  const int c1 = ref_lim > c0 ? min(c0 + p.prefix_chunk, ref_lim) : c0;
+  const int nsub = (c1 - c0) >> 4;
+
+  // block-by-block check of the members' tables against the reference row
+  // over this chunk (at most 64 blocks: the chunk is at most 1024 tokens)
+  const int b0 = c0 / p.block_size;
+  const int nb = nsub > 0 ? (c1 - 1) / p.block_size - b0 + 1 : 0;
+  const size_t mrow = static_cast<size_t>(p.max_blocks_per_seq);
+  int refb = -1;
+  if (lane < nb) refb = p.block_tables[static_cast<size_t>(ref) * mrow + b0 + lane];
+  int ent[NM];
+#pragma unroll
+  for (int mi = 1; mi < NM; ++mi) {
+    const int sq = __builtin_amdgcn_readlane(ms, mi);
+    const int lm = __builtin_amdgcn_readlane(mlim, mi);
+    const int nbm = lm > c0 && nsub > 0 ? (min(c1, lm) - 1) / p.block_size - b0 + 1 : 0;
+    ent[mi] = refb;
+    if (lane < nbm) ent[mi] = p.block_tables[static_cast<size_t>(sq) * mrow + b0 + lane];
+  }
+#pragma unroll
+  for (int mi = 1; mi < NM; ++mi)
+    if (__builtin_amdgcn_ballot_w64(ent[mi] != refb)) mbad = mbad || lane == mi;
+
+  // the columns: member cg*MPC + r/G of this lane's column group cg
+  int lim[CG], seqc[CG];
+  bool cbad[CG];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    const int mi = cg * MPC + r / G;
+    seqc[cg] = __shfl(ms, mi, kWave);
+    lim[cg] = __shfl(mlim, mi, kWave);
+    cbad[cg] = __shfl(static_cast<int>(mbad), mi, kWave) != 0;
+  }
+  const int head = kvh * G + r % G;
+  u32x4 qop[CG][JK];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+#pragma unroll
+    for (int j = 0; j < JK; ++j) {
+      if (lim[cg] > c0 && !cbad[cg]) {
+        qop[cg][j] = *reinterpret_cast<const u32x4*>(
+            p.q + (static_cast<size_t>(seqc[cg]) * p.num_q_heads + head) * D + (kg + 4 * j) * 8);
+      } else {
+        qop[cg][j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  // pool index of the chunk's sub-tiles, one per lane (-1: outside the pool)
+  int tid = 0;
+  if (lane < nsub) {
+    const int tok0 = c0 + 16 * lane;
+    const int blk = tok0 / p.block_size;
+    const int phys = p.block_tables[static_cast<size_t>(ref) * mrow + blk];
+    tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
+              ? (phys * p.num_kv_heads + kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
+              : -1;
+  }
+  bool bad = false;
+  const int koff = (r * D + kg * 8) * 2;
+  const int voff = (4 * kg * D + r * JV) * 2;
+  auto load = [&](int k, Tile<D>& t) {
+    int sub = __builtin_amdgcn_readlane(tid, k);
+    bad |= sub < 0;
+    sub = max(sub, 0);
+    const uint16_t* kt = p.k_cache + static_cast<size_t>(sub) * (16 * D);
+    const uint16_t* vt = p.v_cache + static_cast<size_t>(sub) * (16 * D);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kt), 0, -1, kBufferConfig);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vt), 0, -1, kBufferConfig);
+#pragma unroll
+    for (int j = 0; j < JK; ++j)
+      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 64 * j, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
+  };
+
+  float m[CG], l[CG];
+  f32x4 o[CG][JV];
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    m[cg] = -INFINITY;
+    l[cg] = 0.f;
+#pragma unroll
+    for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // every key of the chunk is a prefix token of the reference; key t counts
+  // for column (cg, r) when t < lim[cg].  A column with no key yet keeps
+  // m = -inf, and its exponents are taken against 0 instead.
+  auto compute = [&](int k, Tile<D>& t) {
+    const int key0 = c0 + 16 * k;
+    u32x2 vop[JV];
+#pragma unroll
+    for (int j = 0; j < JV; ++j) vop[j] = v_operand<D>(t.v, j);
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[cg][j], sc);
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = key0 + 4 * kg + i < lim[cg] ? sc[i] * p.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      bm = max_xor32(max_xor16(bm));
+      const float mn = fmaxf(m[cg], bm);
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float al = fast_exp2(m[cg] - mref);
+      m[cg] = mn;
+      const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mref), fast_exp2(x[1] - mref));
+      const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mref), fast_exp2(x[3] - mref));
+      l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg] * al));
+      if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < JV; ++j) o[cg][j] *= al;
+      }
+      const u32x2 pop = {p01, p23};
+#pragma unroll
+      for (int j = 0; j < JV; ++j) o[cg][j] = Mma<T>::pv(vop[j], pop, o[cg][j]);
+    }
+  };
+
+  if (nsub > 0) {
+    Tile<D> t[2];
+    const int last = nsub - 1;
+    load(0, t[0]);
+    load(min(1, last), t[1]);
+    const int n_pad = (nsub + 1) & ~1;
+    int kb = 0;
+    for (; kb + 2 < n_pad; kb += 2) {
+      compute(kb, t[0]);
+      load(min(kb + 2, last), t[0]);
+      compute(kb + 1, t[1]);
+      load(min(kb + 3, last), t[1]);
+    }
+    compute(kb, t[0]);
+    if (kb + 1 < nsub) compute(kb + 1, t[1]);
+  }
+
+  // lane (kg, r) holds rows 4kg+i of O^T for column r: dims (4kg+i)*JV + j
+  const size_t slot = static_cast<size_t>(p.num_parts) + chunk;
+#pragma unroll
+  for (int cg = 0; cg < CG; ++cg) {
+    float lt = add_xor32(add_xor16(l[cg]));
+    const bool has_keys = lim[cg] > c0 && nsub > 0;
+    // a member this item cannot serve is reported in its chunk-0 state
+    const bool report = cbad[cg] && chunk == 0;
+    if (!has_keys && !report) continue;
+    if (bad || cbad[cg]) lt = __int_as_float(0x7fc00000);
+    const size_t pr = (static_cast<size_t>(seqc[cg]) * p.num_q_heads + head) * p.num_slots + slot;
+    if (kg == 0) {
+      p.part_m[pr] = m[cg];
+      p.part_l[pr] = lt;
+    }
+#pragma unroll
+    for (int j = 0; j < JV; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.part_o[pr * D + (4 * kg + i) * JV + j] = o[cg][j][i];
+  }
+}
+
 // Waves with more sub-tiles than this run the deep register ring (S slots),
 // the others a two-slot ring.
 constexpr int kDeepRingSubTiles = 16;
@@ -177,7 +403,9 @@ constexpr int kDeepRingSubTiles = 16;
 // S and MINW per head size so that nothing spills.  At most three waves per
 // SIMD: with the head_dim 64 tile the allocation would otherwise fit four,
 // which measured slower on the Llama-3.2-1B batch.
-template <typename T, int D, int G, int NW, int S, int MINW>
+// PREFIX: the launch has shared-prefix units (p.prefix_len != nullptr); the
+// kernel without them carries none of their code.
+template <typename T, int D, int G, int NW, int S, int MINW, bool PREFIX>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
 decode_mfma_kernel(DecodeParams p) {
   constexpr int JK = D / 32, JV = D / 16;
@@ -190,21 +418,31 @@ decode_mfma_kernel(DecodeParams p) {
     append_tokens<D, NW * kWave>(p);
     return;
   }
-  const WorkItem w = decode_item(p, blockIdx.x - p.append_wgs, gridDim.x - p.append_wgs);
+  const int pb = static_cast<int>(blockIdx.x) - p.append_wgs;
+  const int prefix_wgs = PREFIX ? p.prefix_wgs : 0;
+  if (PREFIX && pb < prefix_wgs) {
+    // shared-prefix units, one per wave (no workgroup barrier on this path)
+    prefix_unit<T, D, G>(p, xcd_remap(pb, prefix_wgs) * NW + wv);
+    return;
+  }
+  const int nreg = static_cast<int>(gridDim.x) - p.append_wgs - prefix_wgs;
+  const WorkItem w = decode_item(p, pb - prefix_wgs, nreg);
   if (w.seq < 0) return;
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
-  if (bad_len || L == 0) {
+  // positions before pl are the sequence's shared prefix, read by the prefix units
+  const int pl = !PREFIX || bad_len ? 0 : seq_prefix(p, w.seq, L);
+  if (bad_len || L == 0 || pl < 0) {
     // an appended token needs a position: L = 0 with a slot is a caller error
     const bool orphan = p.slot_mapping != nullptr && p.slot_mapping[w.seq] >= 0;
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan);
+    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan || pl < 0);
     return;
   }
-  const int start = w.part * p.part_tokens;
+  const int start = pl + w.part * p.part_tokens;
   if (start >= L) return;
   const int end = min(L, start + p.part_tokens);
   const int nsub = (end - start + 15) >> 4;
-  const int nparts = (L + p.part_tokens - 1) / p.part_tokens;
+  const int nparts = (L - pl + p.part_tokens - 1) / p.part_tokens;
   // this wave owns sub-tiles wv + k*NW, k = 0 .. n_w-1
   const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
 
@@ -423,7 +661,7 @@ decode_mfma_kernel(DecodeParams p) {
       for (int i = 0; i < 4; ++i) sm_o[wv][r][(4 * kg + i) * JV + j] = o[j][i];  // row 4kg+i of O^T is that dim
   }
   __syncthreads();
-  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1);
+  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1 && pl == 0);
 }
 
 }  // namespace pkv

@@ -35,9 +35,9 @@ struct DecodeParams {
   const int32_t* block_tables;   // [B, max_blocks_per_seq]
   const int32_t* context_lens;   // [B]
   uint16_t* out;                 // [B, Hq, D]
-  float* part_o;                 // [B, Hq, num_parts, D]  (only when num_parts > 1)
-  float* part_m;                 // [B, Hq, num_parts]     running max, log2 units
-  float* part_l;                 // [B, Hq, num_parts]     softmax denominator
+  float* part_o;                 // [B, Hq, num_slots, D]  (only when num_slots > 1)
+  float* part_m;                 // [B, Hq, num_slots]     running max, log2 units
+  float* part_l;                 // [B, Hq, num_slots]     softmax denominator
   // Fused append (MFMA kernel only): token i of this step, k_new[i] / v_new[i]
   // ([B, Hkv, D]), goes into slot slot_mapping[i], which must be the slot of
   // position L_i - 1 of sequence i; slot_mapping == nullptr: no append.
@@ -57,6 +57,22 @@ struct DecodeParams {
   int32_t max_blocks_per_seq, max_context_len;
   int32_t part_tokens;           // tokens per partition, a multiple of 16
   int32_t num_parts;             // ceil(max_context_len / part_tokens), >= 1
+  // Shared prefixes (MFMA kernel, 16-bit pools; prefix_len == nullptr: none).
+  // Sequence i's first prefix_len[i] tokens are blocks it shares with the
+  // other members of one prefix item; prefix work units read them once per
+  // item, the regular work items take positions prefix_len[i] .. L_i - 1.
+  // Item k's members are prefix_items[16k .. 16k+15] (-1: unused), member 0
+  // the reference whose block-table row the units read.
+  const int32_t* prefix_len;     // [B]
+  const int32_t* prefix_items;   // [num_prefix_items][16]
+  int32_t num_prefix_items;
+  int32_t max_prefix_len;        // host bound of every prefix_len[i]
+  int32_t prefix_chunk;          // prefix tokens per unit (one wave), multiple of 16, <= 1024
+  int32_t prefix_chunks;         // ceil(max_prefix_len / prefix_chunk), 0 without prefixes
+  int32_t prefix_wgs;            // workgroups of prefix units (after the append ones)
+  // Partial-state slots per (sequence, q head): partitions 0 .. num_parts-1 of
+  // the regular items, then prefix chunk c at slot num_parts + c.
+  int32_t num_slots;
   float scale_log2;              // softmax scale * log2(e) (FP8 pools: times the K scale)
   float out_scale;               // factor on every output (FP8 pools: the V scale; else 1)
 };
@@ -83,6 +99,15 @@ struct PrefillParams {
 constexpr int32_t kMaxPartitionTokens = 8192;
 // Partitions longer than this run with 8 waves per workgroup, shorter ones with 4.
 constexpr int32_t kFourWaveMaxTokens = 4096;
+
+// Column groups of a shared-prefix unit (two at head_dim 64, one at 128, at
+// most G), and so the members of a prefix item: column groups * 16/G <= 16.
+constexpr int prefix_column_groups(int head_dim, int group) {
+  return (head_dim == 64 ? 2 : 1) < group ? (head_dim == 64 ? 2 : 1) : group;
+}
+constexpr int prefix_members_per_item(int head_dim, int group) {
+  return prefix_column_groups(head_dim, group) * (16 / group);
+}
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t stream);
 hipError_t launch_kv_append_fp8(const AppendFp8Params& p, hipStream_t stream);

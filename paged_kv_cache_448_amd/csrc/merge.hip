@@ -1,8 +1,9 @@
 // Merge pass of split-context decode: combine the per-partition softmax
 // states of a sequence into its output with the log-sum-exp identity
-// (see decode_common.h).  One wave per (sequence, q head); lane l owns dims
-// l and l+64.  Partitions are folded in index order, so the result does not
-// depend on which workgroup finished first.
+// (see decode_common.h), together with the states of its shared-prefix chunks
+// when it has one.  One wave per (sequence, q head); lane l owns dims l and
+// l+64.  States are folded in slot order, so the result does not depend on
+// which workgroup finished first.
 //
 // The pages never split a context; this pass exists because on one GPU a few
 // long sequences alone cannot fill 256 compute units.
@@ -20,11 +21,16 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p) {
   if (row >= p.num_seqs * p.num_q_heads) return;
   const int seq = row / p.num_q_heads;
   const int L = p.context_lens[seq];
-  if (bad_length(L, p) || L <= p.part_tokens) return;  // written by the partition kernel
-  const int np = (L + p.part_tokens - 1) / p.part_tokens;
+  if (bad_length(L, p) || L == 0) return;  // written by the partition kernel
+  const int pl = seq_prefix(p, seq, L);
+  if (pl < 0) return;                      // unusable prefix length: NaN written by the partition kernel
+  const int np = (L - pl + p.part_tokens - 1) / p.part_tokens;
+  const int npre = pl > 0 ? (pl + p.prefix_chunk - 1) / p.prefix_chunk : 0;
+  if (np + npre <= 1) return;              // one pass over the whole context wrote the output
 #pragma unroll
   for (int e = 0; e < DV; ++e)
-    p.out[static_cast<size_t>(row) * D + lane + 64 * e] = to_bits<T>(merge_row_elem<D>(p, row, lane + 64 * e, np));
+    p.out[static_cast<size_t>(row) * D + lane + 64 * e] =
+        to_bits<T>(merge_row_elem<D>(p, row, lane + 64 * e, np, npre));
 }
 
 template <typename T, int D>
