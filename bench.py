@@ -576,6 +576,9 @@ def main():
     ap.add_argument("--prefix", default="auto", choices=["auto", "off"],
                     help="read prefix blocks shared by several sequences once per prefix item "
                          "(auto: when the host's block tables share any; off: every sequence reads its own)")
+    ap.add_argument("--work-list", default="auto", choices=["auto", "off"],
+                    help="when the plan splits contexts, launch only the partitions that hold tokens "
+                         "(a host work list, pkv_decode_work_list); off: the full grid")
     ap.add_argument("--kv", default="16bit", choices=["16bit", "fp8"],
                     help="fp8: the step over FP8 (E4M3) pools (append + paged_attn_decode_fp8, fused unless --unfused)")
     args = ap.parse_args()
@@ -670,6 +673,20 @@ def main():
                                               args.partition)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     part = args.partition or pkv.plan_partition(B, c.num_kv_heads, c.block_size, mcl)
+    # split plans: the live (sequence, partition) entries, from the host's lengths
+    work = None
+    if (args.work_list == "auto" and part and args.impl != "simt" and
+            pkv.decode_supported("mfma", c.dtype, c.head_dim, c.group)):
+        wl_np = pkv.decode_work_list(wl.context_lens, c.num_kv_heads, mcl, args.partition,
+                                     None if plan is None else plan.prefix_len)
+        work = torch.from_numpy(wl_np).to(dev)
+        if plan is None:
+            # the prefix entry point with no items is the plain decode; it takes the work list
+            plan = pkv.PrefixPlan(np.zeros(B, np.int32), np.zeros((0, 16), np.int32), 0)
+            pre_len = torch.zeros(B, dtype=torch.int32, device=dev)
+            pre_items = torch.full((1, 16), -1, dtype=torch.int32, device=dev)
+        log(f"work list: {len(wl_np)} live (sequence, partition) entries of {B * -(-mcl // part)} in the grid")
+    shared = plan is not None and plan.num_items > 0
     log(f"rotations R={R} ({R * pool_bytes / 2**30:.2f} GiB of pools), partition plan {part or 'single pass'} tokens, "
         f"workspace {ws_bytes} B, impl {args.impl}")
 
@@ -677,7 +694,7 @@ def main():
         if plan is not None:
             pkv.paged_attn_decode_prefix(t["q"], t["kc"], t["vc"], tables, lens, c.scale, pre_len, pre_items,
                                          plan.max_prefix_len, t["out"], max_context_len=mcl, workspace=ws,
-                                         partition_tokens=args.partition, seq_order=order)
+                                         partition_tokens=args.partition, seq_order=order, work=work)
             return
         pkv.paged_attn_decode(t["q"], t["kc"], t["vc"], tables, lens, c.scale, t["out"], max_context_len=mcl,
                               workspace=ws, partition_tokens=args.partition, impl=args.impl, seq_order=order)
@@ -696,7 +713,7 @@ def main():
                 pkv.paged_attn_decode_prefix(t["q"], t["kc"], t["vc"], tables, lens, c.scale, pre_len, pre_items,
                                              plan.max_prefix_len, t["out"], k_new=t["kn"], v_new=t["vn"],
                                              slot_mapping=slots, max_context_len=mcl, workspace=ws,
-                                             partition_tokens=args.partition, seq_order=order)
+                                             partition_tokens=args.partition, seq_order=order, work=work)
                 continue
             if fused:
                 pkv.append_paged_attn_decode(t["q"], t["kn"], t["vn"], slots, t["kc"], t["vc"], tables, lens, c.scale,
@@ -803,7 +820,7 @@ def main():
     launch_bytes = unique + app if fused else unique  # the fused launch also moves the appended tokens
     dec_gbs = launch_bytes / (dec_us * 1e-6) / 1e9
     log(f"decode bytes {unique / 1e6:.2f} MB unique, {logical / 1e6:.2f} MB logical per layer"
-        + ("" if plan is None else f" (prefix items: the kernels read {per_layer_read(wl, plan, c) / 1e6:.2f} MB)")
+        + ("" if not shared else f" (prefix items: the kernels read {per_layer_read(wl, plan, c) / 1e6:.2f} MB)")
         + "; "
         f"{launch_bytes / 1e6:.2f} MB per launch -> {dec_gbs:.0f} GB/s = {100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak; "
         f"step {value:.0f} GB/s")
@@ -821,10 +838,11 @@ def main():
     traffic = load_traffic(c.name) if fused and plan is None else None
     # bytes the kernels read from the pools: each prefix item's shared blocks
     # once, every sequence's own positions after its prefix
-    read = per_layer_read(wl, plan, c) if plan is not None else logical
+    read = per_layer_read(wl, plan, c) if shared else logical
     if plan is not None:
-        kernel_desc = ("paged_attn_decode_prefix call: partition kernel with prefix units"
-                       + (" (append fused)" if fused else "") + " + merge kernel")
+        kernel_desc = ("paged_attn_decode_prefix call: partition kernel"
+                       + (" with prefix units" if shared else "") + (" (append fused)" if fused else "")
+                       + (" over the live partitions (work list)" if work is not None else "") + " + merge kernel")
     elif fused:
         kernel_desc = ("decode_mfma_kernel with the append fused, one launch per layer" if part == 0 else
                        "append_paged_attn_decode call: partition kernel (append fused) + merge kernel")
@@ -859,8 +877,9 @@ def main():
         "launch_bytes": launch_bytes,
         "decode_bytes_logical": logical,
         "decode_bytes_read": read,
-        "prefix": None if plan is None else {"items": plan.num_items, "max_prefix_len": plan.max_prefix_len,
-                                             "prefix_tokens": int(plan.prefix_len.sum())},
+        "prefix": None if not shared else {"items": plan.num_items, "max_prefix_len": plan.max_prefix_len,
+                                           "prefix_tokens": int(plan.prefix_len.sum())},
+        "work_list_entries": None if work is None else int(work.shape[0]),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(round(traffic)),

@@ -337,6 +337,10 @@ size_t pkv_decode_prefix_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, 
  *   num_prefix_items, max_prefix_len  its counts (host values).  Either 0:
  *                 the plain decode (prefix_len is not read).
  *   workspace     at least pkv_decode_prefix_workspace_bytes(...) bytes.
+ *   work, num_work  NULL / 0, or a device copy of pkv_decode_work_list's
+ *                 output for the same lengths, prefix lengths, max_context_len
+ *                 and partition_tokens: only the partitions listed are
+ *                 launched (in that order; seq_order is then not used).
  *   the other arguments as pkv_append_paged_attn_decode.
  *
  * Sequence i's positions 0 .. prefix_len[i]-1 are read from its item's
@@ -359,7 +363,42 @@ int pkv_paged_attn_decode_prefix(const void* q, const void* k_new, const void* v
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
                                  const int32_t* prefix_len, const int32_t* prefix_items, int32_t num_prefix_items,
                                  int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
-                                 int32_t partition_tokens, const int32_t* seq_order, hipStream_t stream);
+                                 int32_t partition_tokens, const int32_t* seq_order, const int32_t* work,
+                                 int32_t num_work, hipStream_t stream);
+
+/*
+ * pkv_decode_work_list -- the live work of a split decode, one entry per
+ * workgroup, from the host's copy of the lengths, for the work argument of
+ * pkv_paged_attn_decode_prefix.  Host memory only; no device call.
+ *
+ * The split plan gives every sequence as many partitions as the longest
+ * context needs; a launch over that grid also starts the partitions past each
+ * shorter context's end, which find nothing to do but still take a dispatch
+ * slot each.  The list names only the partitions that hold tokens (partition
+ * 0 of every sequence, so empty and invalid sequences still get their zeros
+ * or NaN).  A partition of at most 256 tokens gets one workgroup per 4 or 8
+ * kv heads (the launch's waves per workgroup), each wave taking one kv head
+ * alone; a longer one a workgroup per kv head, its waves sharing the tokens.
+ * Whole sequences are dealt, longest first, to the 8 XCDs' ranges of the
+ * launch so that each gets about equal tokens, and each range is padded to
+ * the same length with entries (-1, 0), which the kernel skips.  Which
+ * workgroup does what changes, not what is computed: each (sequence, kv head,
+ * partition) state is the same arithmetic, and outputs agree with those
+ * without a list to fp32 rounding (identical when no partition is that short).
+ *
+ *   context_lens  [num_seqs] int32, host (the lengths of the decode call)
+ *   prefix_len    NULL, or [num_seqs] int32 host, as pkv_decode_prefix_plan
+ *                 wrote it (partitions then cover only the positions after it)
+ *   num_kv_heads, max_context_len, partition_tokens  as the decode call takes them
+ *   work          [max_work][2] int32, written: (sequence, partition | kv head
+ *                 << 16 | one-wave-per-head << 31)
+ *   num_work      written: entries used, padding included; with PKV_E_SHAPE
+ *                 because max_work is too small, the number needed.
+ * Errors: PKV_E_NULL, PKV_E_SHAPE (max_work too small, bad sizes).
+ */
+int pkv_decode_work_list(const int32_t* context_lens, const int32_t* prefix_len, int32_t num_seqs,
+                         int32_t num_kv_heads, int32_t max_context_len, int32_t partition_tokens, int32_t* work,
+                         int32_t max_work, int32_t* num_work);
 
 /*
  * pkv_decode_supported -- 1 if the decode kernel `impl` (PKV_IMPL_*) is built for

@@ -34,7 +34,7 @@ from ._lib import PKV_BF16, PKV_FP16, PkvError, check, lib  # noqa: F401
 __all__ = ["kv_append", "paged_attn_decode", "append_paged_attn_decode", "decode_workspace_bytes",
            "decode_supported", "plan_partition", "new_cache", "new_cache_fp8", "cache_dims", "kv_append_fp8",
            "paged_attn_decode_fp8", "paged_prefill", "decode_prefix_plan", "decode_prefix_workspace_bytes",
-           "paged_attn_decode_prefix", "PrefixPlan", "BlockAllocator", "PkvError", "lib"]
+           "decode_work_list", "paged_attn_decode_prefix", "PrefixPlan", "BlockAllocator", "PkvError", "lib"]
 
 _DTYPES = {torch.bfloat16: PKV_BF16, torch.float16: PKV_FP16}
 IMPLS = {"auto": 0, "simt": 1, "mfma": 2}
@@ -297,15 +297,38 @@ def decode_prefix_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                        max_context_len, max_prefix_len, partition_tokens))
 
 
+def decode_work_list(context_lens, num_kv_heads, max_context_len, partition_tokens=0, prefix_len=None):
+    """One entry per workgroup of a split decode's live work, from host lengths (and a
+    PrefixPlan's prefix_len), dealt over the XCDs: int32 numpy [n, 2] of (sequence,
+    partition | kv head << 16 | one-wave-per-head << 31); sequence -1 pads."""
+    lens = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    _need(lens.ndim == 1, "context_lens must be one-dimensional")
+    B = int(lens.shape[0])
+    pl = None
+    if prefix_len is not None:
+        pl = np.ascontiguousarray(np.asarray(prefix_len, dtype=np.int32))
+        _need(pl.shape == lens.shape, "prefix_len must have one entry per sequence")
+    args = (lens.ctypes.data, None if pl is None else pl.ctypes.data, B, int(num_kv_heads), int(max_context_len),
+            int(partition_tokens))
+    n = ctypes.c_int32()
+    status = lib().pkv_decode_work_list(*args, None, 0, ctypes.byref(n))  # the size needed
+    if status != 0 and n.value == 0:
+        check(status)
+    work = np.empty((max(n.value, 1), 2), dtype=np.int32)
+    check(lib().pkv_decode_work_list(*args, work.ctypes.data, work.shape[0], ctypes.byref(n)))
+    return work[:n.value].copy()
+
+
 def paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens, scale, prefix_len, prefix_items,
                              max_prefix_len, out=None, *, k_new=None, v_new=None, slot_mapping=None,
-                             max_context_len=None, workspace=None, partition_tokens=0, seq_order=None):
+                             max_context_len=None, workspace=None, partition_tokens=0, seq_order=None, work=None):
     """paged_attn_decode (MFMA kernel) with shared prefixes read once per prefix item,
     optionally with the step's append fused in (k_new, v_new, slot_mapping as in
     append_paged_attn_decode).
 
     prefix_len: int32 [B] and prefix_items: int32 [n, 16], device copies of a
-    PrefixPlan's arrays; max_prefix_len: its host bound.
+    PrefixPlan's arrays; max_prefix_len: its host bound.  work: optional int32
+    [n, 2] device copy of decode_work_list's output for the same arguments.
     """
     N, Hkv, bs, D = cache_dims(k_cache)
     _need(tuple(v_cache.shape) == tuple(k_cache.shape), "k_cache and v_cache differ in shape")
@@ -348,8 +371,16 @@ def paged_attn_decode_prefix(q, k_cache, v_cache, block_tables, context_lens, sc
         _ptr(context_lens), int(max_context_len), ctypes.c_float(scale), _ptr(out), B, Hq, Hkv, D, bs, N,
         _dtype_code(q), _ptr(prefix_len), _ptr(prefix_items), int(prefix_items.shape[0]), int(max_prefix_len),
         _ptr(workspace), ctypes.c_size_t(workspace.numel()), int(partition_tokens), _order_ptr(seq_order, B),
-        _stream(q)))
+        _work_ptr(work), 0 if work is None else int(work.shape[0]), _stream(q)))
     return out
+
+
+def _work_ptr(work):
+    if work is None:
+        return None
+    _device_tensor(work, "work", torch.int32, 2)
+    _need(work.shape[1] == 2, "work must be [n, 2]")
+    return _ptr(work)
 
 
 def paged_prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale, out=None, *,

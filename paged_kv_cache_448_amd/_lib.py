@@ -33,7 +33,8 @@ PROTOTYPES = {
     "pkv_decode_prefix_workspace_bytes": (_c.c_size_t, [_i32] * 8),
     "pkv_paged_attn_decode_prefix": (_c.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _c.c_float, _vp,
                                                 _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _i32, _vp,
-                                                _c.c_size_t, _i32, _vp, _vp]),
+                                                _c.c_size_t, _i32, _vp, _vp, _i32, _vp]),
+    "pkv_decode_work_list": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp]),
     "pkv_decode_supported": (_c.c_int, [_i32] * 4),
     "pkv_paged_prefill": (_c.c_int, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _c.c_float, _vp, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp]),

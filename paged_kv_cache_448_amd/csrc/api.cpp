@@ -89,6 +89,35 @@ int32_t prefix_chunk_count(int32_t max_prefix_len) {
 size_t auto_workspace(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t max_context_len, int32_t prefix_chunks);
 
+// Deal n entries of the given weights (tokens) to the XCDs' contiguous ranges
+// of a launch, heaviest first, each to the group with the least weight so far
+// that has room (group x holds ceil(n/8) entries for x < n % 8, floor(n/8)
+// otherwise, as xcd_remap splits the items); within a group the entries keep
+// the heaviest-first order.  Returns the entry order.
+std::vector<int32_t> deal_to_xcds(const std::vector<int64_t>& weight) {
+  const int32_t n = static_cast<int32_t>(weight.size());
+  std::vector<int32_t> by_w(n);
+  std::iota(by_w.begin(), by_w.end(), 0);
+  std::stable_sort(by_w.begin(), by_w.end(), [&](int32_t a, int32_t b) { return weight[a] > weight[b]; });
+  std::vector<std::vector<int32_t>> groups(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  const int32_t base = n / kXcds, extra = n % kXcds;
+  for (const int32_t e : by_w) {
+    int best = -1;
+    for (int g = 0; g < kXcds; ++g) {
+      const int32_t cap = base + (g < extra ? 1 : 0);
+      if (static_cast<int32_t>(groups[g].size()) >= cap) continue;
+      if (best < 0 || load[g] < load[best]) best = g;
+    }
+    groups[best].push_back(e);
+    load[best] += weight[e] > 0 ? weight[e] : 0;
+  }
+  std::vector<int32_t> order;
+  order.reserve(n);
+  for (const auto& g : groups) order.insert(order.end(), g.begin(), g.end());
+  return order;
+}
+
 // The automatic plan is not monotone in the longest context (a shorter one
 // may be cut into more, smaller partitions), so report the most any longest
 // context up to max_context_len needs: one workspace then serves every later
@@ -171,32 +200,91 @@ int pkv_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t* 
   if (num_seqs < 0) return PKV_E_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!context_lens || !seq_order) return PKV_E_NULL;
-  // Longest context first (ties: lower index first) ...
-  std::vector<int32_t> by_len(num_seqs);
-  std::iota(by_len.begin(), by_len.end(), 0);
-  std::stable_sort(by_len.begin(), by_len.end(),
-                   [&](int32_t a, int32_t b) { return context_lens[a] > context_lens[b]; });
-  // ... each to the XCD group with the fewest tokens so far that still has
-  // room.  Group x holds the work slots the launch's x-th contiguous range of
-  // items covers (xcd_remap): ceil(B/8) slots for the first B % 8 groups,
-  // floor(B/8) for the others.  Within a group the sequences keep the
-  // longest-first order, so each XCD starts its long contexts first.
-  std::vector<std::vector<int32_t>> groups(kXcds);
-  std::vector<int64_t> load(kXcds, 0);
-  const int32_t base = num_seqs / kXcds, extra = num_seqs % kXcds;
-  for (const int32_t s : by_len) {
-    int best = -1;
-    for (int g = 0; g < kXcds; ++g) {
-      const int32_t cap = base + (g < extra ? 1 : 0);
-      if (static_cast<int32_t>(groups[g].size()) >= cap) continue;
-      if (best < 0 || load[g] < load[best]) best = g;
+  // longest context first (ties: lower index first), dealt to the XCD groups
+  std::vector<int64_t> w(num_seqs);
+  for (int32_t i = 0; i < num_seqs; ++i) w[i] = context_lens[i];
+  const std::vector<int32_t> order = deal_to_xcds(w);
+  std::copy(order.begin(), order.end(), seq_order);
+  return PKV_OK;
+}
+
+int pkv_decode_work_list(const int32_t* context_lens, const int32_t* prefix_len, int32_t num_seqs,
+                         int32_t num_kv_heads, int32_t max_context_len, int32_t partition_tokens, int32_t* work,
+                         int32_t max_work, int32_t* num_work) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_kv_heads > 0x7fff || max_context_len < 0 || max_work < 0)
+    return PKV_E_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % 16) return PKV_E_SHAPE;
+  if (!num_work) return PKV_E_NULL;
+  *num_work = 0;
+  if (num_seqs == 0) return PKV_OK;
+  if (!context_lens || (max_work > 0 && !work)) return PKV_E_NULL;
+  // the partition plan and workgroup size the decode call uses for the same sizes
+  const Plan plan = make_plan(num_seqs, num_kv_heads, max_context_len, partition_tokens);
+  if (plan.num_parts > 0xffff) return PKV_E_SHAPE;
+  const int64_t pt = plan.part_tokens;
+  const int32_t nw = pkv::decode_workgroup_waves(plan.num_parts, plan.part_tokens);
+  // entries of sequence i: es[first[i] .. first[i+1]), one per workgroup
+  std::vector<int32_t> first(num_seqs + 1, 0), es, ey;
+  std::vector<int64_t> tokens(num_seqs, 0);
+  for (int32_t i = 0; i < num_seqs; ++i) {
+    const int64_t L = context_lens[i];
+    int64_t pl = prefix_len ? prefix_len[i] : 0;
+    // a length the kernel rejects is answered by partition 0 alone
+    if (pl < 0 || pl % 16 || (pl > 0 && pl > L - 1)) pl = 0;
+    const bool bad = L <= 0 || L > max_context_len;
+    const int64_t n = bad ? 1 : std::min<int64_t>(std::max<int64_t>((L - pl + pt - 1) / pt, 1), plan.num_parts);
+    for (int64_t k = 0; k < n; ++k) {
+      const int64_t toks = bad ? 0 : std::min<int64_t>(pt, L - pl - k * pt);
+      tokens[i] += toks;
+      if (toks <= pkv::kWaveModeMaxTokens) {
+        // wave mode: one workgroup per nw kv heads
+        for (int32_t h = 0; h < num_kv_heads; h += nw) {
+          es.push_back(i);
+          ey.push_back(static_cast<int32_t>(static_cast<uint32_t>(k) | (static_cast<uint32_t>(h) << 16) | (1u << 31)));
+        }
+      } else {
+        for (int32_t h = 0; h < num_kv_heads; ++h) {
+          es.push_back(i);
+          ey.push_back(static_cast<int32_t>(static_cast<uint32_t>(k) | (static_cast<uint32_t>(h) << 16)));
+        }
+      }
     }
-    groups[best].push_back(s);
-    load[best] += context_lens[s] > 0 ? context_lens[s] : 0;
+    first[i + 1] = static_cast<int32_t>(es.size());
   }
-  int32_t k = 0;
-  for (const auto& g : groups)
-    for (const int32_t s : g) seq_order[k++] = s;
+  // Whole sequences dealt to the 8 XCD groups by tokens (longest first, to the
+  // group with the fewest tokens so far, then the fewest entries), each
+  // group's entries padded with skipped entries (sequence -1) to the largest
+  // group's count, so that xcd_remap's equal ranges are the groups.  Keeping a
+  // sequence's partitions on one XCD measured faster than dealing partitions
+  // one by one (long contexts in 1536-token partitions: 39.9 us against 46.1
+  // per launch).
+  std::vector<int32_t> by(num_seqs);
+  std::iota(by.begin(), by.end(), 0);
+  std::stable_sort(by.begin(), by.end(), [&](int32_t a, int32_t b) { return tokens[a] > tokens[b]; });
+  std::vector<std::vector<int32_t>> g(kXcds);
+  std::vector<int64_t> load(kXcds, 0);
+  for (const int32_t sq : by) {
+    int best = 0;
+    for (int x = 1; x < kXcds; ++x)
+      if (load[x] < load[best] || (load[x] == load[best] && g[x].size() < g[best].size())) best = x;
+    for (int32_t e = first[sq]; e < first[sq + 1]; ++e) g[best].push_back(e);
+    load[best] += tokens[sq];
+  }
+  size_t mx = 0;
+  for (const auto& v : g) mx = std::max(mx, v.size());
+  if (static_cast<int64_t>(mx) * kXcds > INT_MAX) return PKV_E_SHAPE;
+  if (static_cast<int64_t>(mx) * kXcds > max_work) {
+    *num_work = static_cast<int32_t>(mx * kXcds);  // the size needed
+    return PKV_E_SHAPE;
+  }
+  size_t k = 0;
+  for (const auto& v : g)
+    for (size_t j = 0; j < mx; ++j) {
+      work[2 * k] = j < v.size() ? es[v[j]] : -1;
+      work[2 * k + 1] = j < v.size() ? ey[v[j]] : 0;
+      ++k;
+    }
+  *num_work = static_cast<int32_t>(k);
   return PKV_OK;
 }
 
@@ -256,7 +344,8 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
                 void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                 int32_t block_size, int32_t num_blocks, int32_t dtype, void* workspace, size_t workspace_bytes,
                 int32_t partition_tokens, int32_t impl, const FusedAppend& app, const Fp8Scales* fp8,
-                const int32_t* seq_order, hipStream_t stream, const PrefixDesc* pre = nullptr) {
+                const int32_t* seq_order, hipStream_t stream, const PrefixDesc* pre = nullptr,
+                const int32_t* work = nullptr, int32_t num_work = 0) {
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       max_context_len < 0)
     return PKV_E_SHAPE;
@@ -297,6 +386,9 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   if (prefixed && (!use_mfma || fp8)) return PKV_E_UNSUPPORTED;  // shared prefixes: MFMA kernel, 16-bit pools
   if (num_seqs == 0) return PKV_OK;
   if (prefixed && (!pre->prefix_len || !pre->prefix_items)) return PKV_E_NULL;
+  if (num_work < 0) return PKV_E_SHAPE;
+  if (num_work > 0 && (!use_mfma || fp8)) return PKV_E_UNSUPPORTED;  // work lists: MFMA kernel, 16-bit pools
+  if (num_work > 0 && !work) return PKV_E_NULL;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out) return PKV_E_NULL;
   if (fused && (!app.k_new || !app.v_new)) return PKV_E_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return PKV_E_SHAPE;
@@ -334,7 +426,8 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.k_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
   p.v_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   p.append_wgs = 0;  // set by the MFMA launcher for fused calls
-  p.seq_order = seq_order;
+  p.seq_order = num_work > 0 ? nullptr : seq_order;  // the work list carries the order
+
   p.num_seqs = num_seqs;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -345,14 +438,17 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.max_context_len = max_context_len;
   p.part_tokens = plan.part_tokens;
   p.num_parts = plan.num_parts;
-  p.prefix_len = prefixed ? pre->prefix_len : nullptr;
-  p.prefix_items = prefixed ? pre->prefix_items : nullptr;
-  p.num_prefix_items = prefixed ? pre->num_items : 0;
-  p.max_prefix_len = prefixed ? pre->max_prefix_len : 0;
-  p.prefix_chunk = prefixed ? prefix_chunk_tokens(pre->max_prefix_len) : 0;
-  p.prefix_chunks = chunks;
-  p.prefix_wgs = 0;  // set by the MFMA launcher
-  p.num_slots = plan.num_parts + chunks;
+  pkv::DecodeExt x{};
+  x.prefix_len = prefixed ? pre->prefix_len : nullptr;
+  x.prefix_items = prefixed ? pre->prefix_items : nullptr;
+  x.num_prefix_items = prefixed ? pre->num_items : 0;
+  x.max_prefix_len = prefixed ? pre->max_prefix_len : 0;
+  x.prefix_chunk = prefixed ? prefix_chunk_tokens(pre->max_prefix_len) : 0;
+  x.prefix_chunks = chunks;
+  x.prefix_wgs = 0;  // set by the MFMA launcher
+  x.num_slots = plan.num_parts + chunks;
+  x.work = num_work > 0 ? work : nullptr;
+  x.num_work = num_work > 0 ? num_work : 0;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * (fp8 ? fp8->k : 1.0) * kLog2e);
   p.out_scale = fp8 ? fp8->v : 1.f;
   // the fused FP8 append encodes x * (1 / scale), exactly as pkv_kv_append_fp8
@@ -360,11 +456,11 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.v_inv_scale = fp8 ? 1.f / fp8->v : 1.f;
 
   hipError_t e = fp8        ? pkv::launch_decode_fp8(p, dtype, stream)
-                 : use_mfma ? pkv::launch_decode_mfma(p, dtype, stream)
+                 : use_mfma ? pkv::launch_decode_mfma(p, x, dtype, stream)
                             : pkv::launch_decode_simt(p, dtype, stream);
   if (e != hipSuccess) return PKV_E_HIP;
   if (plan.num_parts + chunks > 1) {
-    e = pkv::launch_merge(p, dtype, stream);
+    e = pkv::launch_merge(p, x, dtype, stream);
     if (e != hipSuccess) return PKV_E_HIP;
   }
   return PKV_OK;
@@ -618,12 +714,13 @@ int pkv_paged_attn_decode_prefix(const void* q, const void* k_new, const void* v
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t dtype,
                                  const int32_t* prefix_len, const int32_t* prefix_items, int32_t num_prefix_items,
                                  int32_t max_prefix_len, void* workspace, size_t workspace_bytes,
-                                 int32_t partition_tokens, const int32_t* seq_order, hipStream_t stream) {
+                                 int32_t partition_tokens, const int32_t* seq_order, const int32_t* work,
+                                 int32_t num_work, hipStream_t stream) {
   const PrefixDesc pre{prefix_len, prefix_items, num_prefix_items, max_prefix_len};
   return decode_call(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, dtype, workspace,
                      workspace_bytes, partition_tokens, PKV_IMPL_MFMA, FusedAppend{k_new, v_new, slot_mapping},
-                     nullptr, seq_order, stream, &pre);
+                     nullptr, seq_order, stream, &pre, work, num_work);
 }
 
 }  // extern "C"

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
       for (int i = 0; i < 4; ++i) sm_o[wv][r][(4 * kg + i) * JV + j] = o[j][i];  // row 4kg+i of O^T is that dim
   }
   __syncthreads();
-  combine_and_store<T, D, G, NW, true>(sm_m, sm_l, sm_o, p, w, nparts == 1);
+  combine_and_store<T, D, G, NW, true>(sm_m, sm_l, sm_o, p, w, nparts == 1, p.num_parts);
 }
 
 // Sub-tiles in flight per wave, measured on the Llama-3.2-1B batch and the

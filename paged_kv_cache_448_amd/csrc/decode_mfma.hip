@@ -19,11 +19,12 @@ template <> struct MfmaShape<128> { static constexpr int kDepth = 2, kMinWaves =
 // workgroup, shorter partitions with 4 (each wave may own at most 64
 // sub-tiles of a partition).
 template <typename T, int D, int G>
-hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_t(const DecodeParams& p, const DecodeExt& x, hipStream_t stream) {
   constexpr int S = MfmaShape<D>::kDepth, W = MfmaShape<D>::kMinWaves;
-  int64_t items = static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
+  int64_t items = x.work != nullptr ? static_cast<int64_t>(x.num_work)
+                                     : static_cast<int64_t>(p.num_seqs) * p.num_parts * p.num_kv_heads;
   if (p.part_tokens > kMaxPartitionTokens) return hipErrorInvalidValue;
-  const int nw = (p.num_parts == 1 || p.part_tokens > kFourWaveMaxTokens) ? 8 : 4;
+  const int nw = decode_workgroup_waves(p.num_parts, p.part_tokens);
   DecodeParams q = p;
   q.append_wgs = 0;
   if (p.slot_mapping != nullptr) {
@@ -36,47 +37,48 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
     q.append_wgs = static_cast<int32_t>(wgs);
     items += wgs;
   }
-  q.prefix_wgs = 0;
-  if (p.prefix_len != nullptr) {
+  DecodeExt xq = x;
+  xq.prefix_wgs = 0;
+  if (x.prefix_len != nullptr) {
     // shared-prefix units, one per wave, in a multiple of 8 workgroups (as the
     // append ones) right after the append workgroups
-    const int64_t units = static_cast<int64_t>(p.num_prefix_items) * p.num_kv_heads * p.prefix_chunks;
+    const int64_t units = static_cast<int64_t>(x.num_prefix_items) * p.num_kv_heads * x.prefix_chunks;
     const int64_t wgs = ((units + nw - 1) / nw + 7) / 8 * 8;
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    q.prefix_wgs = static_cast<int32_t>(wgs);
+    xq.prefix_wgs = static_cast<int32_t>(wgs);
     items += wgs;
   }
   if (items > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(items));
-  if (p.prefix_len != nullptr) {
+  if (x.prefix_len != nullptr || x.work != nullptr) {
     if (nw == 8) {
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W, true>), grid, dim3(8 * kWave), 0, stream, q);
+      hipLaunchKernelGGL((decode_mfma_ext_kernel<T, D, G, 8, S, W>), grid, dim3(8 * kWave), 0, stream, q, xq);
     } else {
-      hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W, true>), grid, dim3(4 * kWave), 0, stream, q);
+      hipLaunchKernelGGL((decode_mfma_ext_kernel<T, D, G, 4, S, W>), grid, dim3(4 * kWave), 0, stream, q, xq);
     }
   } else if (nw == 8) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W, false>), grid, dim3(8 * kWave), 0, stream, q);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 8, S, W>), grid, dim3(8 * kWave), 0, stream, q);
   } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W, false>), grid, dim3(4 * kWave), 0, stream, q);
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, G, 4, S, W>), grid, dim3(4 * kWave), 0, stream, q);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_g(const DecodeParams& p, int group, hipStream_t stream) {
+hipError_t launch_g(const DecodeParams& p, const DecodeExt& x, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_t<T, D, 1>(p, stream);
-    case 2: return launch_t<T, D, 2>(p, stream);
-    case 4: return launch_t<T, D, 4>(p, stream);
-    case 8: return launch_t<T, D, 8>(p, stream);
-    case 16: return launch_t<T, D, 16>(p, stream);
+    case 1: return launch_t<T, D, 1>(p, x, stream);
+    case 2: return launch_t<T, D, 2>(p, x, stream);
+    case 4: return launch_t<T, D, 4>(p, x, stream);
+    case 8: return launch_t<T, D, 8>(p, x, stream);
+    case 16: return launch_t<T, D, 16>(p, x, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <typename T>
-hipError_t launch_d(const DecodeParams& p, int group, hipStream_t stream) {
-  return p.head_dim == 64 ? launch_g<T, 64>(p, group, stream) : launch_g<T, 128>(p, group, stream);
+hipError_t launch_d(const DecodeParams& p, const DecodeExt& x, int group, hipStream_t stream) {
+  return p.head_dim == 64 ? launch_g<T, 64>(p, x, group, stream) : launch_g<T, 128>(p, x, group, stream);
 }
 
 }  // namespace
@@ -87,9 +89,9 @@ bool mfma_supported(int dtype, int head_dim, int group) {
   return group == 1 || group == 2 || group == 4 || group == 8 || group == 16;
 }
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeParams& p, const DecodeExt& x, int dtype, hipStream_t stream) {
   const int group = p.num_q_heads / p.num_kv_heads;
-  return dtype == 0 ? launch_d<Bf16>(p, group, stream) : launch_d<Fp16>(p, group, stream);
+  return dtype == 0 ? launch_d<Bf16>(p, x, group, stream) : launch_d<Fp16>(p, x, group, stream);
 }
 
 }  // namespace pkv

@@ -190,27 +190,27 @@ __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
 // non-finite V value in a reference block past a member's prefix length would
 // reach that member; cached values are finite.
 template <typename T, int D, int G>
-__device__ __forceinline__ void prefix_unit(const DecodeParams& p, int unit) {
+__device__ __forceinline__ void prefix_unit(const DecodeParams& p, const DecodeExt& x, int unit) {
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int CG = prefix_column_groups(D, G);
   constexpr int MPC = 16 / G;     // members per column group
   constexpr int NM = CG * MPC;    // members per item, <= 16
   const int lane = threadIdx.x & (kWave - 1);
   const int r = lane & 15, kg = lane >> 4;
-  const int chunk = unit % p.prefix_chunks;
-  unit /= p.prefix_chunks;
+  const int chunk = unit % x.prefix_chunks;
+  unit /= x.prefix_chunks;
   const int kvh = unit % p.num_kv_heads;
   const int item = unit / p.num_kv_heads;
-  if (item >= p.num_prefix_items) return;
-  const int32_t* mem = p.prefix_items + static_cast<size_t>(item) * 16;
-  const int c0 = chunk * p.prefix_chunk;
+  if (item >= x.num_prefix_items) return;
+  const int32_t* mem = x.prefix_items + static_cast<size_t>(item) * 16;
+  const int c0 = chunk * x.prefix_chunk;
 
   // the reference member and its usable prefix length (-1: unusable)
   const int ref = mem[0];
   int ref_lim = -1;
   if (static_cast<unsigned>(ref) < static_cast<unsigned>(p.num_seqs)) {
     const int Lr = p.context_lens[ref];
-    if (!bad_length(Lr, p)) ref_lim = seq_prefix(p, ref, Lr);
+    if (!bad_length(Lr, p)) ref_lim = seq_prefix(x, ref, Lr);
   }
 
   // lane mi < NM: member mi's sequence and prefix length; mlim = 0: no prefix
@@ -222,7 +222,7 @@ __device__ __forceinline__ void prefix_unit(const DecodeParams& p, int unit) {
     const int sq = mem[lane];
     if (static_cast<unsigned>(sq) < static_cast<unsigned>(p.num_seqs)) {
       const int L = p.context_lens[sq];
-      const int pl = bad_length(L, p) ? 0 : seq_prefix(p, sq, L);
+      const int pl = bad_length(L, p) ? 0 : seq_prefix(x, sq, L);
       if (pl > 0) {
         ms = sq;
         mlim = pl;
@@ -235,7 +235,7 @@ __device__ __forceinline__ void prefix_unit(const DecodeParams& p, int unit) {
     // members this item cannot serve
     if (chunk != 0) return;
   }
-  const int c1 = ref_lim > c0 ? min(c0 + p.prefix_chunk, ref_lim) : c0;
+  const int c1 = ref_lim > c0 ? min(c0 + x.prefix_chunk, ref_lim) : c0;
   const int nsub = (c1 - c0) >> 4;
 
   // block-by-block check of the members' tables against the reference row
@@ -383,7 +383,7 @@ __device__ __forceinline__ void prefix_unit(const DecodeParams& p, int unit) {
     const bool report = cbad[cg] && chunk == 0;
     if (!has_keys && !report) continue;
     if (bad || cbad[cg]) lt = __int_as_float(0x7fc00000);
-    const size_t pr = (static_cast<size_t>(seqc[cg]) * p.num_q_heads + head) * p.num_slots + slot;
+    const size_t pr = (static_cast<size_t>(seqc[cg]) * p.num_q_heads + head) * x.num_slots + slot;
     if (kg == 0) {
       p.part_m[pr] = m[cg];
       p.part_l[pr] = lt;
@@ -403,11 +403,11 @@ constexpr int kDeepRingSubTiles = 16;
 // S and MINW per head size so that nothing spills.  At most three waves per
 // SIMD: with the head_dim 64 tile the allocation would otherwise fit four,
 // which measured slower on the Llama-3.2-1B batch.
-// PREFIX: the launch has shared-prefix units (p.prefix_len != nullptr); the
-// kernel without them carries none of their code.
-template <typename T, int D, int G, int NW, int S, int MINW, bool PREFIX>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
-decode_mfma_kernel(DecodeParams p) {
+// EXT: the launch may have shared-prefix units (x.prefix_len), a work list
+// (x.work) and wave-mode entries; the kernel without them carries none of
+// their code (the plain decode keeps its registers and instruction stream).
+template <typename T, int D, int G, int NW, int S, bool EXT>
+__device__ __forceinline__ void decode_body(const DecodeParams& p, const DecodeExt& x) {
   constexpr int JK = D / 32, JV = D / 16;
   __shared__ float sm_m[NW][G], sm_l[NW][G], sm_o[NW][G][D];
 
@@ -419,23 +419,36 @@ decode_mfma_kernel(DecodeParams p) {
     return;
   }
   const int pb = static_cast<int>(blockIdx.x) - p.append_wgs;
-  const int prefix_wgs = PREFIX ? p.prefix_wgs : 0;
+  constexpr bool PREFIX = EXT;
+  const int prefix_wgs = PREFIX ? x.prefix_wgs : 0;
   if (PREFIX && pb < prefix_wgs) {
     // shared-prefix units, one per wave (no workgroup barrier on this path)
-    prefix_unit<T, D, G>(p, xcd_remap(pb, prefix_wgs) * NW + wv);
+    prefix_unit<T, D, G>(p, x, xcd_remap(pb, prefix_wgs) * NW + wv);
     return;
   }
   const int nreg = static_cast<int>(gridDim.x) - p.append_wgs - prefix_wgs;
-  const WorkItem w = decode_item(p, pb - prefix_wgs, nreg);
+  WorkItem w = decode_item<EXT>(p, pb - prefix_wgs, nreg, x);
   if (w.seq < 0) return;
+  // Wave mode (a short partition from a work list): wave wv takes kv head
+  // kvh + wv alone, all the partition's sub-tiles, and stores its own state;
+  // no wave of such a workgroup reaches a workgroup barrier.
+  const bool wmode = EXT && w.wave;
+  if (wmode) {
+    w.kvh += wv;
+    if (w.kvh >= p.num_kv_heads) return;
+  }
   const int L = p.context_lens[w.seq];
   const bool bad_len = bad_length(L, p);
   // positions before pl are the sequence's shared prefix, read by the prefix units
-  const int pl = !PREFIX || bad_len ? 0 : seq_prefix(p, w.seq, L);
+  const int pl = !PREFIX || bad_len ? 0 : seq_prefix(x, w.seq, L);
   if (bad_len || L == 0 || pl < 0) {
     // an appended token needs a position: L = 0 with a slot is a caller error
     const bool orphan = p.slot_mapping != nullptr && p.slot_mapping[w.seq] >= 0;
-    write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan || pl < 0);
+    if (wmode) {
+      write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan || pl < 0, lane, kWave);
+    } else {
+      write_degenerate<T, G, NW * kWave>(p, w, bad_len || orphan || pl < 0);
+    }
     return;
   }
   const int start = pl + w.part * p.part_tokens;
@@ -443,8 +456,11 @@ decode_mfma_kernel(DecodeParams p) {
   const int end = min(L, start + p.part_tokens);
   const int nsub = (end - start + 15) >> 4;
   const int nparts = (L - pl + p.part_tokens - 1) / p.part_tokens;
-  // this wave owns sub-tiles wv + k*NW, k = 0 .. n_w-1
-  const int n_w = wv < nsub ? (nsub - wv + NW - 1) / NW : 0;
+  // this wave owns sub-tiles sb + k*ss, k = 0 .. n_w-1: wv + k*NW, or in wave
+  // mode all of them (at most the 64 a wave holds ids for: more is an error)
+  const int sb = wmode ? 0 : wv, ss = wmode ? 1 : NW;
+  const bool too_long = wmode && nsub > kWave;
+  const int n_w = wmode ? min(nsub, kWave) : (wv < nsub ? (nsub - wv + NW - 1) / NW : 0);
 
   // Q^T operand: column r = q head kvh*G + r (zero for r >= G), dims of run kg + 4j
   u32x4 qop[JK];
@@ -480,14 +496,14 @@ decode_mfma_kernel(DecodeParams p) {
   // when the table names a block outside the pool.
   int tid = 0;
   if (lane < n_w) {
-    const int tok0 = start + 16 * (wv + lane * NW);
+    const int tok0 = start + 16 * (sb + lane * ss);
     const int blk = tok0 / p.block_size;
     const int phys = p.block_tables[static_cast<size_t>(w.seq) * p.max_blocks_per_seq + blk];
     tid = static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_blocks)
               ? (phys * p.num_kv_heads + w.kvh) * (p.block_size >> 4) + ((tok0 - blk * p.block_size) >> 4)
               : -1;
   }
-  bool bad = false;
+  bool bad = too_long;
 
   // Fused append of the token decoded this step, which sits at position L-1.
   // Its K and V were read together with the block-table window, so the
@@ -500,18 +516,21 @@ decode_mfma_kernel(DecodeParams p) {
   // so nothing before the first loads waits for that block id; a slot that is
   // not the slot of L-1 is not written and makes the sequence's output NaN
   // (every workgroup of the sequence checks).
-  __shared__ __align__(16) uint16_t sm_new[2][D];  // the appended token's K and V
-  int app_w = -1, app_k = -1, app_r = 0;           // wave, step and token row that hold it
+  // the appended token's K and V; one copy per wave in wave mode, where the
+  // waves hold different kv heads
+  __shared__ __align__(16) uint16_t sm_new[EXT ? NW : 1][2][D];
+  const int sw = EXT ? wv : 0;            // this wave's copy
+  int app_w = -1, app_k = -1, app_r = 0;  // wave, step and token row that hold it
   if (p.slot_mapping != nullptr && app_slot >= 0) {
     const int app_pos = L - 1;
     if (app_pos >= start && app_pos < end) {
       app_r = app_pos & 15;  // the block size is a multiple of 16
       const int s_tok = (app_pos - start) >> 4;
-      app_w = s_tok % NW;
-      app_k = s_tok / NW;
+      app_w = wmode ? wv : s_tok % NW;
+      app_k = wmode ? s_tok : s_tok / NW;
       if (wv == app_w) {
-        if (lane < D / 8) *reinterpret_cast<u32x4*>(&sm_new[0][8 * lane]) = krun;
-        if (lane < 16) *reinterpret_cast<VSlice<D>*>(&sm_new[1][JV * lane]) = vrun;
+        if (lane < D / 8) *reinterpret_cast<u32x4*>(&sm_new[sw][0][8 * lane]) = krun;
+        if (lane < 16) *reinterpret_cast<VSlice<D>*>(&sm_new[sw][1][JV * lane]) = vrun;
         // the same wave reads the rows back in its compute step
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -557,12 +576,12 @@ decode_mfma_kernel(DecodeParams p) {
       // token row app_r of this sub-tile is the appended token
       if (r == app_r) {
 #pragma unroll
-        for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(&sm_new[0][(4 * j + kg) * 8]);
+        for (int j = 0; j < JK; ++j) t.k[j] = *reinterpret_cast<const u32x4*>(&sm_new[sw][0][(4 * j + kg) * 8]);
       }
       if ((app_r >> 2) == kg) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if ((app_r & 3) == i) t.v[i] = *reinterpret_cast<const VSlice<D>*>(&sm_new[1][r * JV]);
+          if ((app_r & 3) == i) t.v[i] = *reinterpret_cast<const VSlice<D>*>(&sm_new[sw][1][r * JV]);
       }
     }
     u32x2 vop[JV];
@@ -571,7 +590,7 @@ decode_mfma_kernel(DecodeParams p) {
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[j], sc);
-    const int nvalid = k < n_w ? min(16, end - (start + 16 * (wv + k * NW))) : 0;
+    const int nvalid = k < n_w ? min(16, end - (start + 16 * (sb + k * ss))) : 0;
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 4 * kg + i < nvalid ? sc[i] * p.scale_log2 : -INFINITY;
@@ -650,6 +669,41 @@ decode_mfma_kernel(DecodeParams p) {
   // fold the four token rows (kg) of the denominator
   l = add_xor32(add_xor16(l));
   if (bad) l = __int_as_float(0x7fc00000);
+  if (wmode) {
+    // the wave's state is the partition's: lane (kg, r) holds rows 4kg+i of
+    // O^T for column r, i.e. dims (4kg+i)*JV + j of q head kvh*G + r
+    if (r < G) {
+      const size_t row = static_cast<size_t>(w.seq) * p.num_q_heads + w.kvh * G + r;
+      if (nparts == 1 && pl == 0) {
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t wd[JV / 2];
+#pragma unroll
+          for (int j = 0; j < JV / 2; ++j)
+            wd[j] = static_cast<uint32_t>(to_bits<T>(o[2 * j][i] * inv)) |
+                    (static_cast<uint32_t>(to_bits<T>(o[2 * j + 1][i] * inv)) << 16);
+          uint16_t* dst = p.out + row * D + (4 * kg + i) * JV;
+          if constexpr (JV == 4) {
+            *reinterpret_cast<u32x2*>(dst) = u32x2{wd[0], wd[1]};
+          } else {
+            *reinterpret_cast<u32x4*>(dst) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+          }
+        }
+      } else {
+        const size_t pr = row * x.num_slots + w.part;
+        if (kg == 0) {
+          p.part_m[pr] = m;
+          p.part_l[pr] = l;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < JV; ++j) p.part_o[pr * D + (4 * kg + i) * JV + j] = o[j][i];
+      }
+    }
+    return;
+  }
   if (r < G) {
     if (kg == 0) {
       sm_m[wv][r] = m;
@@ -661,7 +715,20 @@ decode_mfma_kernel(DecodeParams p) {
       for (int i = 0; i < 4; ++i) sm_o[wv][r][(4 * kg + i) * JV + j] = o[j][i];  // row 4kg+i of O^T is that dim
   }
   __syncthreads();
-  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1 && pl == 0);
+  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, nparts == 1 && pl == 0, EXT ? x.num_slots : p.num_parts);
+}
+
+template <typename T, int D, int G, int NW, int S, int MINW>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
+decode_mfma_kernel(DecodeParams p) {
+  decode_body<T, D, G, NW, S, false>(p, DecodeExt{});
+}
+
+// The same with the launch's extensions (shared prefixes, a work list).
+template <typename T, int D, int G, int NW, int S, int MINW>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, NW * kWave), amdgpu_waves_per_eu(MINW, 3))) void
+decode_mfma_ext_kernel(DecodeParams p, DecodeExt x) {
+  decode_body<T, D, G, NW, S, true>(p, x);
 }
 
 }  // namespace pkv

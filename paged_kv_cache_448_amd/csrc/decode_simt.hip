@@ -164,7 +164,7 @@ __global__ __launch_bounds__(NW * kWave) void decode_simt_kernel(DecodeParams p)
     for (int e = 0; e < DV; ++e) sm_o[wv][h][lane + 64 * e] = acc[h][e];
   }
   __syncthreads();
-  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, single);
+  combine_and_store<T, D, G, NW>(sm_m, sm_l, sm_o, p, w, single, p.num_parts);
 }
 
 constexpr int kSimtWaves = 4;

@@ -35,9 +35,9 @@ struct DecodeParams {
   const int32_t* block_tables;   // [B, max_blocks_per_seq]
   const int32_t* context_lens;   // [B]
   uint16_t* out;                 // [B, Hq, D]
-  float* part_o;                 // [B, Hq, num_slots, D]  (only when num_slots > 1)
-  float* part_m;                 // [B, Hq, num_slots]     running max, log2 units
-  float* part_l;                 // [B, Hq, num_slots]     softmax denominator
+  float* part_o;                 // [B, Hq, slots, D]  (only when slots > 1): slots = num_parts,
+  float* part_m;                 // [B, Hq, slots]     or DecodeExt::num_slots; running max (log2 units)
+  float* part_l;                 // [B, Hq, slots]     softmax denominator
   // Fused append (MFMA kernel only): token i of this step, k_new[i] / v_new[i]
   // ([B, Hkv, D]), goes into slot slot_mapping[i], which must be the slot of
   // position L_i - 1 of sequence i; slot_mapping == nullptr: no append.
@@ -57,6 +57,15 @@ struct DecodeParams {
   int32_t max_blocks_per_seq, max_context_len;
   int32_t part_tokens;           // tokens per partition, a multiple of 16
   int32_t num_parts;             // ceil(max_context_len / part_tokens), >= 1
+  float scale_log2;              // softmax scale * log2(e) (FP8 pools: times the K scale)
+  float out_scale;               // factor on every output (FP8 pools: the V scale; else 1)
+};
+
+// Extensions of the MFMA decode launch (shared prefixes, work lists), a
+// second kernel argument of the kernel that takes them: the plain decode's
+// argument block stays as small as it is (a larger one measured 0.3 us slower
+// per launch on the Llama-3.2-1B batch).  Zero-initialised: none.
+struct DecodeExt {
   // Shared prefixes (MFMA kernel, 16-bit pools; prefix_len == nullptr: none).
   // Sequence i's first prefix_len[i] tokens are blocks it shares with the
   // other members of one prefix item; prefix work units read them once per
@@ -73,8 +82,14 @@ struct DecodeParams {
   // Partial-state slots per (sequence, q head): partitions 0 .. num_parts-1 of
   // the regular items, then prefix chunk c at slot num_parts + c.
   int32_t num_slots;
-  float scale_log2;              // softmax scale * log2(e) (FP8 pools: times the K scale)
-  float out_scale;               // factor on every output (FP8 pools: the V scale; else 1)
+  // Work list (optional, MFMA kernel): one entry per workgroup, replacing the
+  // (slot, partition, kv head) grid, so partitions past a sequence's end are
+  // never launched.  Entry e: work[2e] = sequence (-1: skip), work[2e+1] =
+  // partition | kv head << 16 | wave mode << 31.  In wave mode wave w takes
+  // kv head + w of the partition alone (at most 64 sub-tiles), with no
+  // workgroup barrier.  nullptr: the full grid.
+  const int32_t* work;
+  int32_t num_work;
 };
 
 // Paged prefill: the new tokens of every sequence, packed (sequence i's at rows
@@ -99,6 +114,14 @@ struct PrefillParams {
 constexpr int32_t kMaxPartitionTokens = 8192;
 // Partitions longer than this run with 8 waves per workgroup, shorter ones with 4.
 constexpr int32_t kFourWaveMaxTokens = 4096;
+// Waves per workgroup of the MFMA decode launch: eight for a single pass or
+// partitions above kFourWaveMaxTokens, four for shorter partitions.
+constexpr int decode_workgroup_waves(int32_t num_parts, int32_t part_tokens) {
+  return (num_parts == 1 || part_tokens > kFourWaveMaxTokens) ? 8 : 4;
+}
+// Partitions of at most this many tokens go to wave mode in a work list
+// (at most 64 sub-tiles: a wave holds one sub-tile id per lane).
+constexpr int32_t kWaveModeMaxTokens = 256;
 
 // Column groups of a shared-prefix unit (two at head_dim 64, one at 128, at
 // most G), and so the members of a prefix item: column groups * 16/G <= 16.
@@ -116,14 +139,16 @@ bool simt_supported(int dtype, int head_dim, int group);
 hipError_t launch_decode_simt(const DecodeParams& p, int dtype, hipStream_t stream);
 
 bool mfma_supported(int dtype, int head_dim, int group);
-hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, const DecodeExt& x, int dtype, hipStream_t stream);
 
 // FP8 (E4M3) pools (k_cache / v_cache hold one code per element); no fused append.
 hipError_t launch_decode_fp8(const DecodeParams& p, int dtype, hipStream_t stream);
 
 hipError_t launch_prefill_mfma(const PrefillParams& p, int dtype, hipStream_t stream);
 
-hipError_t launch_merge(const DecodeParams& p, int dtype, hipStream_t stream);
+// x: the extensions of the decode launch before it (shared prefixes; its
+// partial-state slots per row)
+hipError_t launch_merge(const DecodeParams& p, const DecodeExt& x, int dtype, hipStream_t stream);
 
 // Size of the device scratch of the allocation-free decode entry point
 // (split-context partial states): 16 MiB per GPU.

@@ -46,7 +46,7 @@ def _dev_plan(plan):
     return torch.from_numpy(plan.prefix_len).cuda(), torch.from_numpy(np.ascontiguousarray(items)).cuda()
 
 
-def _run(wl, layer, plan, fused, pt=0, prefix_len=None, seq_order=None, num_items=None):
+def _run(wl, layer, plan, fused, pt=0, prefix_len=None, seq_order=None, num_items=None, work=None):
     """One prefix decode of `layer` on fresh device pools; returns (out bits, k pool bits, v pool bits)."""
     c = wl.cfg
     dw = upload(wl, layers=[layer])
@@ -67,7 +67,8 @@ def _run(wl, layer, plan, fused, pt=0, prefix_len=None, seq_order=None, num_item
         kw = {}
     out = pkv.paged_attn_decode_prefix(d.q, d.k_cache, d.v_cache, dw.tables, dw.lens, c.scale, pl, items,
                                        plan.max_prefix_len, max_context_len=max(int(wl.context_lens.max()), 0),
-                                       partition_tokens=pt, seq_order=seq_order, **kw)
+                                       partition_tokens=pt, seq_order=seq_order,
+                                       work=None if work is None else torch.from_numpy(work).cuda(), **kw)
     res = to_bits(out), to_bits(d.k_cache).ravel(), to_bits(d.v_cache).ravel()
     del dw, d
     return res
@@ -250,3 +251,90 @@ def test_wrong_plans_give_nan_for_their_sequences_only():
         saw_nan |= bool(expect)
         print(f"{what}: NaN sequences {nan_seqs}; the others max|err| {e:.2e}", flush=True)
     assert saw_nan
+
+
+def _agree_ratio(a_bits, b_bits, dtype):
+    """|a - b| against the bound for two work splits of the same inputs: each
+    probability is rounded to the 16-bit type against a running maximum that
+    depends on the split (the decode tests' plan-agreement bound, 8u absolute)."""
+    a, b = bits_to_f64(a_bits, dtype), bits_to_f64(b_bits, dtype)
+    ulp = 2.0 ** -7 if dtype == "bf16" else 2.0 ** -10
+    u = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -12
+    return float((np.abs(a - b) / (8 * u + ulp * np.abs(b))).max())
+
+
+@pytest.mark.parametrize("cid,pt", [(5, 0), (5, 256), (3, 0), (3, 512), (2, 128), (1, 16), (4, 256)])
+def test_work_list(cid, pt):
+    """Launching only the live partitions (the host's work list, short ones one
+    wave per kv head): against the oracle, the pools bit-identical to the
+    oracle's append, and the outputs within the plan-agreement bound of the
+    full grid's, with and without shared prefixes."""
+    wl = _wl5() if cid == 5 else workloads.build(cid)
+    c = wl.cfg
+    mcl = int(wl.context_lens.max())
+    plans = [_plan(wl)]
+    if plans[0].num_items:
+        plans.append(pkv.PrefixPlan(np.zeros_like(plans[0].prefix_len), plans[0].items[:0], 0))
+    kc, vc = oracle_caches(wl, 0)
+    ref = oracle_decode(wl, 0, kc, vc)
+    for plan in plans:
+        pl = plan.prefix_len if plan.num_items else None
+        work = pkv.decode_work_list(wl.context_lens, c.num_kv_heads, mcl, pt, pl)
+        full = _run(wl, 0, plan, True, pt)
+        listed = _run(wl, 0, plan, True, pt, work=work)
+        assert np.array_equal(listed[1], kc) and np.array_equal(listed[2], vc), "pools"
+        r, e = assert_parity(listed[0], ref, c.dtype, f"config {cid} partition {pt} items {plan.num_items}")
+        agree = _agree_ratio(listed[0], full[0], c.dtype)
+        waves = int(((work[:, 1].astype(np.int64) & 0xffffffff) >> 31).sum())
+        print(f"config {cid} partition {pt} items {plan.num_items}: {len(work)} workgroups ({waves} in wave mode), "
+              f"max|err| {e:.2e}, agreement with the full grid {agree:.3f}", flush=True)
+        assert agree <= 1.0
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"{s[0]}q{s[1]}kv-d{s[2]}-bs{s[3]}-{s[4]}")
+def test_work_list_shapes(shape):
+    """Wave mode and the work list on every GQA size, both head dims, block
+    sizes to 1024, forced partitions, with shared prefixes, fused and not."""
+    Hq, Hkv, D, bs, dt, groups, pb = shape
+    edges = [0, 1, 2, 17, bs, bs + 1, 2 * bs, 2 * bs + 1, 3 * bs + 1, pb * bs, pb * bs + 1, pb * bs + 2,
+             (pb + 1) * bs + 1, (pb + 3) * bs + 5]
+    lens = np.array([e for _ in range(groups) for e in edges])
+    wl = _shared(Hq, Hkv, D, bs, lens, groups, pb, dt, seed=3)
+    plan = _plan(wl)
+    mcl = int(wl.context_lens.max())
+    kc, vc = oracle_caches(wl, 0)
+    ref = oracle_decode(wl, 0, kc, vc)
+    for pt in (0, 16, 48, 512):
+        work = pkv.decode_work_list(wl.context_lens, Hkv, mcl, pt, plan.prefix_len if plan.num_items else None)
+        for fused in (False, True):
+            out, kg, vg = _run(wl, 0, plan, fused, pt, work=work)
+            if fused:
+                assert np.array_equal(kg, kc) and np.array_equal(vg, vc)
+            r, e = assert_parity(out, ref, dt, f"{shape} partition {pt} fused {fused} work list")
+        print(f"{shape} partition {pt}: {len(work)} workgroups, max|err| {e:.2e}", flush=True)
+
+
+def test_work_list_degenerate_sequences():
+    """Empty sequences and lengths past the bound: partition 0 alone answers
+    them (zeros, NaN), as in the full grid; the others agree with it."""
+    wl = workloads.custom(16, 4, 64, 16, [0, 300, 1, 0, 2000, 17], "bf16", seed=2)
+    lens = wl.context_lens.copy()
+    lens[4] = 3000  # past max_context_len (the tables' 2000 tokens): NaN
+    plan = _plan(wl)
+    work = pkv.decode_work_list(lens, 4, 2000, 256)
+    dw = upload(wl, layers=[0])
+    d = dw.layers[0]
+    poison_tails_gpu(wl, d)
+    pkv.kv_append(d.k_new, d.v_new, dw.slots, d.k_cache, d.v_cache)
+    lens_d = torch.from_numpy(lens).cuda()
+    pl, items = _dev_plan(plan)
+    outs = []
+    for w in (None, torch.from_numpy(work).cuda()):
+        outs.append(to_bits(pkv.paged_attn_decode_prefix(d.q, d.k_cache, d.v_cache, dw.tables, lens_d, wl.cfg.scale,
+                                                         pl, items, 0, max_context_len=2000, partition_tokens=256,
+                                                         work=w)))
+    got = bits_to_f64(outs[1], "bf16")
+    assert np.all(got[0] == 0) and np.all(got[3] == 0) and np.all(np.isnan(got[4]))
+    assert np.array_equal(outs[0][[0, 3, 4]], outs[1][[0, 3, 4]])
+    live = [1, 2, 5]
+    assert _agree_ratio(outs[1][live], outs[0][live], "bf16") <= 1.0

@@ -165,20 +165,20 @@ def test_plan_errors():
 
 def _decode_prefix(**kw):
     a = dict(q=16, kn=None, vn=None, sm=None, kc=16, vc=16, bt=16, mb=4, cl=16, mcl=64, scale=0.125, out=16, B=2,
-             Hq=4, Hkv=2, D=64, bs=16, N=8, dt=0, pl=16, items=16, ni=1, mpl=32, ws=None, wsb=0, pt=0)
+             Hq=4, Hkv=2, D=64, bs=16, N=8, dt=0, pl=16, items=16, ni=1, mpl=32, ws=None, wsb=0, pt=0, work=None, nw=0)
     a.update(kw)
     p = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
     return pkv.lib().pkv_paged_attn_decode_prefix(
         p(a["q"]), p(a["kn"]), p(a["vn"]), p(a["sm"]), p(a["kc"]), p(a["vc"]), p(a["bt"]), a["mb"], p(a["cl"]),
         a["mcl"], ctypes.c_float(a["scale"]), p(a["out"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["N"],
         a["dt"], p(a["pl"]), p(a["items"]), a["ni"], a["mpl"], p(a["ws"]), ctypes.c_size_t(a["wsb"]), a["pt"],
-        None, None)
+        None, p(a["work"]), a["nw"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(pl=None), E_NULL), (dict(items=None), E_NULL), (dict(ni=-1), E_SHAPE), (dict(mpl=-16), E_SHAPE),
     (dict(mpl=65), E_SHAPE), (dict(D=96), E_UNSUPPORTED), (dict(Hq=6, Hkv=4), E_SHAPE),
-    (dict(ws=None, wsb=0), -4),
+    (dict(ws=None, wsb=0), -4), (dict(nw=-1), E_SHAPE), (dict(nw=3, work=None), E_NULL),
 ])
 def test_decode_prefix_rejects_before_launch(kw, status):
     assert _decode_prefix(**kw) == status
@@ -198,3 +198,90 @@ def test_decode_prefix_workspace():
         w = pkv.decode_prefix_workspace_bytes(2, 4, 2, 64, 16, 8192, mpl, 8192)
         rows = 2 * 4 * (1 + chunks)
         assert w == align(rows * 64 * 4) + 2 * align(rows * 4), (mpl, chunks)
+
+
+def _decode_entries(work, Hkv, nw):
+    """(seq, part, kv head, wave mode) per workgroup, wave-mode entries expanded to their heads."""
+    out = []
+    for s_, y in np.asarray(work, dtype=np.int64):
+        y &= 0xffffffff
+        part, h, mode = int(y & 0xffff), int((y >> 16) & 0x7fff), int(y >> 31)
+        if s_ < 0:
+            assert y == 0, "padding entries are (-1, 0)"
+            continue
+        heads = range(h, min(h + nw, Hkv)) if mode else [h]
+        out += [(int(s_), part, hh, mode) for hh in heads]
+    return out
+
+
+def test_work_list_covers_live_partitions_once():
+    """Every sequence's partition 0 and each partition that holds tokens, for
+    every kv head, once; nothing past a context's end; partitions of at most
+    256 tokens in wave mode (one wave per head), longer ones a workgroup per head."""
+    for seed in range(20):
+        rng = np.random.default_rng(seed)
+        B = int(rng.integers(1, 300))
+        lens = rng.integers(0, 6000, size=B).astype(np.int32)
+        lens[rng.random(B) < 0.05] = 0
+        Hkv = int(rng.choice([1, 2, 8, 12]))
+        mcl = int(lens.max()) if B else 0
+        pt_req = int(rng.choice([0, 256, 1536]))
+        pt = pkv.plan_partition(B, Hkv, 16, mcl) if pt_req == 0 else pt_req
+        part_tokens = pt if pt and pt < mcl else max(16, (mcl + 15) // 16 * 16)
+        nparts = max(1, -(-mcl // part_tokens))
+        nw = 8 if nparts == 1 or part_tokens > 4096 else 4
+        pl = None
+        if seed % 2:
+            pl = (rng.integers(0, 40, size=B) * 16).astype(np.int32)
+            pl = np.where(pl <= lens - 1, pl, 0).astype(np.int32)
+        work = pkv.decode_work_list(lens, Hkv, mcl, pt_req, pl)
+        assert len(work) % 8 == 0, "eight equal ranges"
+        ent = _decode_entries(work, Hkv, nw)
+        got = [(s_, part, h) for s_, part, h, _ in ent]
+        assert len(set(got)) == len(got), seed
+        expect = set()
+        for i, L in enumerate(lens):
+            p0 = 0 if pl is None else int(pl[i])
+            n = max(1, -(-(int(L) - p0) // part_tokens)) if L > 0 else 1
+            expect |= {(i, k, h) for k in range(n) for h in range(Hkv)}
+        assert set(got) == expect, seed
+        for s_, part, h, mode in ent:
+            L = int(lens[s_])
+            p0 = 0 if pl is None else int(pl[s_])
+            toks = max(0, min(part_tokens, L - p0 - part * part_tokens)) if L > 0 else 0
+            assert mode == (toks <= 256), (seed, s_, part, toks, mode)
+
+
+def test_work_list_balances_xcds():
+    lens = np.array([5000, 100, 3000, 3000, 20, 1536, 1537, 4000] * 8, dtype=np.int32)
+    work = pkv.decode_work_list(lens, 8, 5000, 1536)
+    n = len(work) // 8
+    loads, seqs = [], []
+    for g in range(8):
+        ent = _decode_entries(work[g * n:(g + 1) * n], 8, 4)
+        seqs.append({s_ for s_, _, _, _ in ent})
+        loads.append(sum(min(1536, int(lens[s_]) - part * 1536) for s_, part, _, _ in ent) // 8)
+    for g in range(8):
+        for o in range(g + 1, 8):
+            assert not seqs[g] & seqs[o], "a sequence on one XCD"
+    assert max(loads) - min(loads) <= int(lens.max()), loads
+
+
+def test_work_list_small():
+    w = pkv.decode_work_list(np.array([5], np.int32), 1, 16, 0)
+    # one 5-token partition: wave mode (bit 31), kv head 0
+    assert [tuple(int(v) for v in x) for x in w] == [(0, -(1 << 31))] + [(-1, 0)] * 7
+    # equal loads: the group with fewer entries, so the two land on two XCDs
+    w = pkv.decode_work_list(np.array([0, 0], np.int32), 2, 0, 0)
+    assert [int(x[0]) for x in w] == [0, 1] + [-1] * 6
+
+
+def test_work_list_errors():
+    lens = np.array([100, 2000], dtype=np.int32)
+    w = np.zeros((1, 2), dtype=np.int32)
+    n = ctypes.c_int32()
+    assert pkv.lib().pkv_decode_work_list(lens.ctypes.data, None, 2, 2, 2000, 256, w.ctypes.data, 1,
+                                          ctypes.byref(n)) == E_SHAPE
+    assert pkv.lib().pkv_decode_work_list(lens.ctypes.data, None, 2, 2, 2000, 24, w.ctypes.data, 1,
+                                          ctypes.byref(n)) == E_SHAPE
+    assert pkv.lib().pkv_decode_work_list(None, None, 2, 2, 2000, 256, w.ctypes.data, 1, ctypes.byref(n)) == E_NULL
