@@ -69,11 +69,12 @@ size_t workspace_for(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, co
   return align256(rows * head_dim * sizeof(float)) + 2 * align256(rows * sizeof(float));
 }
 
-// Tokens of a shared prefix one prefix unit (a wave) takes: about a quarter
-// of the longest prefix, so its units spread over four times as many waves,
-// between 64 and 1024 tokens (a wave holds the ids of at most 64 sub-tiles).
+// Tokens of a shared prefix one prefix unit (a wave) takes: half the longest
+// prefix, between 64 and 1024 tokens (a wave holds the ids of at most 64
+// sub-tiles).  On the 16-layer step (512-token prefixes) halves measured
+// 42.4 us per layer, whole prefixes 44.4, quarters 43.6 and eighths 49.8.
 int32_t prefix_chunk_tokens(int32_t max_prefix_len) {
-  int32_t c = (max_prefix_len + 3) / 4;
+  int32_t c = (max_prefix_len + 1) / 2;
   c = (c + 15) / 16 * 16;
   return c < 64 ? 64 : (c > 1024 ? 1024 : c);
 }

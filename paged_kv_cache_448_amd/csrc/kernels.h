@@ -120,7 +120,8 @@ constexpr int decode_workgroup_waves(int32_t num_parts, int32_t part_tokens) {
   return (num_parts == 1 || part_tokens > kFourWaveMaxTokens) ? 8 : 4;
 }
 // Partitions of at most this many tokens go to wave mode in a work list
-// (at most 64 sub-tiles: a wave holds one sub-tile id per lane).
+// (at most 64 sub-tiles: a wave holds one sub-tile id per lane).  On the
+// 16-layer step 256 measured best (128: +0.4 us, 512: +4.6, 1024: +9.3 per layer).
 constexpr int32_t kWaveModeMaxTokens = 256;
 
 // Column groups of a shared-prefix unit (two at head_dim 64, one at 128, at

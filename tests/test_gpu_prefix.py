@@ -165,7 +165,7 @@ def test_shapes_block_edges_partitions(shape):
 
 
 def test_long_prefixes_several_chunks():
-    """Prefixes of up to 2400 tokens: 608-token prefix chunks, up to four per member."""
+    """Prefixes of up to 2400 tokens: 1024-token prefix chunks, up to three per member."""
     bs, pb = 16, 150
     lens = np.array([2400 + 1, 2400 + 2, 3000, 2400 + 16, 1000, 2401, 4000, 33, 1600, 2500, 2417, 2402] * 2)
     wl = _shared(32, 8, 64, bs, lens, 2, pb, "bf16", seed=5)

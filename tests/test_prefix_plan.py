@@ -189,12 +189,12 @@ def test_decode_prefix_workspace():
     plain = pkv.decode_workspace_bytes(64, 32, 8, 64, 16, 2048)
     assert plain == 0
     w = pkv.decode_prefix_workspace_bytes(64, 32, 8, 64, 16, 2048, 512)
-    rows = 64 * 32 * (1 + 4)  # one pass + four prefix chunks of 128 tokens
+    rows = 64 * 32 * (1 + 2)  # one pass + two prefix chunks of 256 tokens
     align = lambda n: (n + 255) // 256 * 256  # noqa: E731
     assert w == align(rows * 64 * 4) + 2 * align(rows * 4)
     assert pkv.decode_prefix_workspace_bytes(64, 32, 8, 64, 16, 2048, 0) == plain
-    # chunk = a quarter of the longest prefix in multiples of 16, clamped to [64, 1024]
-    for mpl, chunks in ((16, 1), (64, 1), (100, 2), (256, 4), (257, 4), (4096, 4), (8000, 8)):
+    # chunk = half the longest prefix in multiples of 16, clamped to [64, 1024]
+    for mpl, chunks in ((16, 1), (64, 1), (100, 2), (256, 2), (257, 2), (2400, 3), (4096, 4), (8000, 8)):
         w = pkv.decode_prefix_workspace_bytes(2, 4, 2, 64, 16, 8192, mpl, 8192)
         rows = 2 * 4 * (1 + chunks)
         assert w == align(rows * 64 * 4) + 2 * align(rows * 4), (mpl, chunks)
