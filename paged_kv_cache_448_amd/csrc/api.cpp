@@ -424,8 +424,6 @@ int decode_call(const void* q, const void* k_cache, const void* v_cache, const i
   p.k_new = static_cast<const uint16_t*>(app.k_new);
   p.v_new = static_cast<const uint16_t*>(app.v_new);
   p.slot_mapping = app.slot_mapping;
-  p.k_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(k_cache)) : nullptr;
-  p.v_cache_w = fused ? static_cast<uint16_t*>(const_cast<void*>(v_cache)) : nullptr;
   p.append_wgs = 0;  // set by the MFMA launcher for fused calls
   p.seq_order = num_work > 0 ? nullptr : seq_order;  // the work list carries the order
 

@@ -94,8 +94,8 @@ __device__ __forceinline__ void v_operands(const VCodes<D> (&v)[4], u32x2 (&op)[
 template <typename T, int D, int NT>
 __device__ __forceinline__ void append_tokens_fp8(const DecodeParams& p) {
   constexpr int runs = D / 8;
-  uint8_t* kc = reinterpret_cast<uint8_t*>(p.k_cache_w);
-  uint8_t* vc = reinterpret_cast<uint8_t*>(p.v_cache_w);
+  uint8_t* kc = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_cache));
+  uint8_t* vc = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_cache));
   const int64_t total = static_cast<int64_t>(p.num_seqs) * p.num_kv_heads * runs;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x; i < total;
        i += static_cast<int64_t>(p.append_wgs) * NT) {

@@ -138,7 +138,8 @@ __device__ __forceinline__ u32x2 v_operand(const VSlice<D> (&v)[4], int j) {
   return u32x2{__builtin_amdgcn_perm(v[1].w[w], v[0].w[w], sel), __builtin_amdgcn_perm(v[3].w[w], v[2].w[w], sel)};
 }
 
-// Fused append, store side: the same bytes kv_append writes for token i =
+// Fused append, store side (the pools are writable for fused calls; the
+// parameter block keeps them const to stay small): the same bytes kv_append writes for token i =
 // sequence i, after the checks the decode side makes (a valid length, and the
 // slot is the slot of position L_i - 1); thread per (token, kv head, 8-dim run)
 // as in kv_append, grid-strided over the append workgroups.  A token's K and V
@@ -164,8 +165,8 @@ __device__ __forceinline__ void append_tokens(const DecodeParams& p) {
         slot != static_cast<int64_t>(phys) * p.block_size + off)
       continue;
     const size_t row = ((static_cast<size_t>(phys) * p.num_kv_heads + h) * p.block_size + off) * D + c * 8;
-    *reinterpret_cast<u32x4*>(p.k_cache_w + row) = *reinterpret_cast<const u32x4*>(p.k_new + th * D + c * 8);
-    *reinterpret_cast<u32x4*>(p.v_cache_w + row) = *reinterpret_cast<const u32x4*>(p.v_new + th * D + c * 8);
+    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + row) = *reinterpret_cast<const u32x4*>(p.k_new + th * D + c * 8);
+    *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_cache) + row) = *reinterpret_cast<const u32x4*>(p.v_new + th * D + c * 8);
   }
 }
 

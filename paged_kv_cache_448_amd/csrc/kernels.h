@@ -43,9 +43,7 @@ struct DecodeParams {
   // position L_i - 1 of sequence i; slot_mapping == nullptr: no append.
   const uint16_t* k_new;
   const uint16_t* v_new;
-  const int64_t* slot_mapping;
-  uint16_t* k_cache_w;           // the same pools, writable
-  uint16_t* v_cache_w;
+  const int64_t* slot_mapping;   // (the append writes through k_cache and v_cache)
   int32_t append_wgs;            // leading workgroups that store the appended tokens (fused append), else 0
   // Fused append into FP8 pools: the reciprocals of the pool scales, as
   // kv_append_fp8 multiplies by them (unused otherwise).
