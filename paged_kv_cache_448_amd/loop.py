@@ -98,6 +98,7 @@ class DecodeLoop:
         self._next = 0
         self._lib = lib()
         self.host_wait_s = 0.0  # time the host spent waiting for the GPU to free a staging buffer
+        self.prefix_steps = 0   # steps whose decode read shared prefixes once per prefix item
 
     def _staging(self):
         st = self._ring[self._next]
@@ -192,6 +193,7 @@ class DecodeLoop:
         # prefix item; a split plan launches only its live partitions.  Both are planned
         # here from the host's tables and lengths, outside the launches.
         items_n, max_pl = self._plan_prefixes(st, tables, lens, M)
+        self.prefix_steps += items_n > 0
         # (without shared prefixes the full grid in dispatch order measured 2% faster on the
         # 256-sequence loop than the work list)
         work_n = self._plan_work(st, lens, lens_max, True) if items_n else 0

@@ -129,5 +129,7 @@ def test_prefix_cached_loop_matches_replay(seed):
             gpu.finish(rid)
             rep.finish(rid, lc.num_layers)
     assert total_cached > 0, "the groups' prefixes should have been shared"
+    assert gpu.prefix_steps > 0, "some steps' decode should have read shared prefixes once per prefix item"
     assert gpu.alloc.num_free == lc.num_blocks
-    print(f"seed {seed}: {total_cached} prompt tokens served from shared blocks", flush=True)
+    print(f"seed {seed}: {total_cached} prompt tokens served from shared blocks; {gpu.prefix_steps} steps "
+          f"decoded with prefix items", flush=True)
