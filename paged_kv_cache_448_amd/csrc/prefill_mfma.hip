@@ -21,15 +21,18 @@
 //   S^T[16 keys x 16 cols] = K . Q^T    (D/32 mfma 16x16x32 per group)
 //   O^T[D x 16 cols]      += V^T . P^T  (D/16 mfma 16x16x16 per group)
 //
+// At head_dim 64 the sub-tiles go in pairs, and P.V takes both at once: D/16
+// mfma 16x16x32 over 32 keys per group (half the matrix-core time of the
+// 16x16x16 products).
+//
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
 // as in decode; the running reference is moved only when a score exceeds it by
 // more than a fixed slack, so most sub-tiles need no rescaling of the
 // accumulators (the result is the same: softmax does not depend on the
-// shift); each lane tests its own four scores against it and the column
-// maxima are folded across lanes only when a test fires.  A key is visible
-// to a column when it is not after the
-// column's position; sub-tiles entirely before the wave's first position need
-// no mask.  Every wave sees every key its columns need, so nothing is combined
+// shift); each lane tests its own scores against the matching threshold in
+// score units and the column maxima are folded across lanes only when a test
+// fires.  A key is visible to a column when it is not after the column's
+// position; sub-tiles entirely before the wave's first position need no mask.  Every wave sees every key its columns need, so nothing is combined
 // across waves: each lane divides and stores its columns' outputs itself.
 //
 // Work items: (sequence, kv head, chunk of NW * CG * 16/G new tokens), the
@@ -48,17 +51,23 @@ namespace {
 constexpr float kRescaleSlack = 8.f;
 
 // Column groups per wave (accumulators of 64 VGPRs at either head_dim), key
-// sub-tiles in flight per wave, and workgroups per CU.  Two workgroups of
-// four waves give each wave 256 registers; at head_dim 128 a second sub-tile
-// in flight does not fit them and would spill, so that kernel loads one
-// sub-tile ahead only.
+// sub-tiles (kPairs: pairs of them) in flight per wave, and workgroups per CU.
+// Two workgroups of four waves give each wave 256 registers.  Measured on the
+// prompt batches: deeper rings, a third workgroup per CU (three column groups)
+// and pairs at head_dim 128 were no faster.
 template <int D> struct PrefillShape;
-template <> struct PrefillShape<64> { static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2; };
-template <> struct PrefillShape<128> { static constexpr int kGroups = 2, kDepth = 1, kBlocksPerCu = 2; };
+template <> struct PrefillShape<64> {
+  static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2;
+  static constexpr bool kPairs = true;
+};
+template <> struct PrefillShape<128> {
+  static constexpr int kGroups = 2, kDepth = 2, kBlocksPerCu = 2;
+  static constexpr bool kPairs = false;
+};
 
 constexpr int kPrefillWaves = 4;
 
-template <typename T, int D, int G, int NW, int CG, int S>
+template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
@@ -106,6 +115,9 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   const int nsub = (p0 + last_tok + 1 + 15) >> 4;
   const int unmasked = (p0 + first + 1) >> 4;    // sub-tiles before this are visible to every column
 
+  // the scale is positive (checked by the caller), so a score above a
+  // threshold is a probability above the threshold's
+  const float sc2 = p.scale_log2;  // softmax scale * log2(e)
   int pos[CG];
   u32x4 qop[CG][JK];
 #pragma unroll
@@ -154,11 +166,14 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
   };
 
-  float m[CG], l[CG];
+  // thr: the score above which a probability would exceed 2^kRescaleSlack,
+  // (m + kRescaleSlack) / scale in score units
+  float m[CG], l[CG], thr[CG];
   f32x4 o[CG][JV];
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     m[cg] = -INFINITY;
+    thr[cg] = -INFINITY;
     l[cg] = 0.f;
 #pragma unroll
     for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -193,22 +208,23 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
       }
       // lazy rescaling: the reference m moves only when a score exceeds it by
       // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack;
-      // each lane checks its own scores, the column maxima are folded across
-      // lanes only when one exceeds
-      const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__builtin_amdgcn_ballot_w64(lm * p.scale_log2 > m[cg] + kRescaleSlack)) {
-        const float bm = max_xor32(max_xor16(lm)) * p.scale_log2;
+      // each lane compares its own scores with the threshold, the column
+      // maxima are folded across lanes only when one exceeds it
+      if (__builtin_amdgcn_ballot_w64(x[0] > thr[cg] || x[1] > thr[cg] || x[2] > thr[cg] || x[3] > thr[cg])) {
+        const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        const float bm = max_xor32(max_xor16(lm)) * sc2;
         const bool up = bm > m[cg] + kRescaleSlack;
         const float mn = up ? bm : m[cg];
         const float al = fast_exp2(m[cg] - mn);
         m[cg] = mn;
+        thr[cg] = (mn + kRescaleSlack) / sc2;
         l[cg] *= al;
 #pragma unroll
         for (int j = 0; j < JV; ++j) o[cg][j] *= al;
       }
       const float nm = -m[cg];
-      const uint32_t p01 = Mma<T>::pack(fast_exp2(fmaf(x[0], p.scale_log2, nm)), fast_exp2(fmaf(x[1], p.scale_log2, nm)));
-      const uint32_t p23 = Mma<T>::pack(fast_exp2(fmaf(x[2], p.scale_log2, nm)), fast_exp2(fmaf(x[3], p.scale_log2, nm)));
+      const uint32_t p01 = Mma<T>::pack(fast_exp2(fmaf(x[0], sc2, nm)), fast_exp2(fmaf(x[1], sc2, nm)));
+      const uint32_t p23 = Mma<T>::pack(fast_exp2(fmaf(x[2], sc2, nm)), fast_exp2(fmaf(x[3], sc2, nm)));
       l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg]));
       const u32x2 pop = {p01, p23};
 #pragma unroll
@@ -216,20 +232,131 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     }
   };
 
-  {
+  // P.V over a pair of key sub-tiles (32 keys) in one 16x16x32 product per 16
+  // dims, which the matrix cores run at twice the rate of two 16x16x16 ones.
+  // Lane group kg holds keys 4kg..4kg+3 of the first sub-tile and then
+  // 4kg..4kg+3 of the second: the order of the keys inside one product is
+  // free as long as the V and P operands agree.  Both sub-tiles' scores share
+  // one softmax reference.
+  auto compute2 = [&](int q, Tile<D>& ta, Tile<D>& tb, auto causal) {
+    const int key0 = 32 * q;
+    u32x4 vop[JV];
+    {
+      u32x2 va[JV], vb[JV];
+#pragma unroll
+      for (int j = 0; j < JV; ++j) {
+        va[j] = v_operand<D>(ta.v, j);
+        vb[j] = v_operand<D>(tb.v, j);
+      }
+      if (key0 + 32 > L) {
+        // keys past the context (the last block's tail) may hold anything: zero their V
+        const int na = L - key0, nb = L - key0 - 16;
+        const uint32_t a0 = (4 * kg < na ? 0xffffu : 0u) | (4 * kg + 1 < na ? 0xffff0000u : 0u);
+        const uint32_t a1 = (4 * kg + 2 < na ? 0xffffu : 0u) | (4 * kg + 3 < na ? 0xffff0000u : 0u);
+        const uint32_t b0 = (4 * kg < nb ? 0xffffu : 0u) | (4 * kg + 1 < nb ? 0xffff0000u : 0u);
+        const uint32_t b1 = (4 * kg + 2 < nb ? 0xffffu : 0u) | (4 * kg + 3 < nb ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < JV; ++j) {
+          va[j].x &= a0;
+          va[j].y &= a1;
+          vb[j].x &= b0;
+          vb[j].y &= b1;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < JV; ++j) vop[j] = u32x4{va[j].x, va[j].y, vb[j].x, vb[j].y};
+    }
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < JK; ++j) sa = Mma<T>::qk(ta.k[j], qop[cg][j], sa);
+#pragma unroll
+      for (int j = 0; j < JK; ++j) sb = Mma<T>::qk(tb.k[j], qop[cg][j], sb);
+      float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      if constexpr (decltype(causal)::value) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = key0 + (i >> 2) * 16 + 4 * kg + (i & 3) <= pos[cg] ? x[i] : -INFINITY;
+      }
+      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      if (__builtin_amdgcn_ballot_w64(lm > thr[cg])) {
+        const float bm = max_xor32(max_xor16(lm)) * sc2;
+        const bool up = bm > m[cg] + kRescaleSlack;
+        const float mn = up ? bm : m[cg];
+        const float al = fast_exp2(m[cg] - mn);
+        m[cg] = mn;
+        thr[cg] = (mn + kRescaleSlack) / sc2;
+        l[cg] *= al;
+#pragma unroll
+        for (int j = 0; j < JV; ++j) o[cg][j] *= al;
+      }
+      const float nm = -m[cg];
+      uint32_t pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pw[i] = Mma<T>::pack(fast_exp2(fmaf(x[2 * i], sc2, nm)), fast_exp2(fmaf(x[2 * i + 1], sc2, nm)));
+      l[cg] = Mma<T>::sum2(pw[3], Mma<T>::sum2(pw[2], Mma<T>::sum2(pw[1], Mma<T>::sum2(pw[0], l[cg]))));
+      const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+      for (int j = 0; j < JV; ++j) o[cg][j] = Mma<T>::qk(vop[j], pop, o[cg][j]);
+    }
+  };
+
+  if constexpr (PAIRS) {
+    // S pairs in flight.  Pair q is sub-tiles 2q and 2q+1; a pair with a
+    // masked sub-tile runs the causal variant, so does the last pair when it
+    // has a single sub-tile (its second one, past the wave's last position,
+    // is a masked copy of the last).
+    const int npair = (nsub + 1) >> 1;
+    const int upair = unmasked >> 1;
+    Tile<D> t[2 * S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      load(2 * i, t[2 * i]);
+      load(2 * i + 1, t[2 * i + 1]);
+    }
+    const int n_pad = (npair + S - 1) / S * S;
+    int qb = 0;
+    for (; qb + S <= upair && qb + S < n_pad; qb += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        compute2(qb + i, t[2 * i], t[2 * i + 1], std::false_type{});
+        load(2 * (qb + i + S), t[2 * i]);
+        load(2 * (qb + i + S) + 1, t[2 * i + 1]);
+      }
+    }
+    for (; qb + S < n_pad; qb += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        compute2(qb + i, t[2 * i], t[2 * i + 1], std::true_type{});
+        load(2 * (qb + i + S), t[2 * i]);
+        load(2 * (qb + i + S) + 1, t[2 * i + 1]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (qb + i < npair) compute2(qb + i, t[2 * i], t[2 * i + 1], std::true_type{});
+  } else {
     Tile<D> t[S];
 #pragma unroll
     for (int i = 0; i < S; ++i) load(i, t[i]);
     const int n_pad = (nsub + S - 1) / S * S;
     int kb = 0;
+    // Rounds before the first sub-tile that some column must not fully see
+    // run without the causal mask, the rest with it: two loops rather than a
+    // choice per step, whose merging paths cost register copies of every
+    // accumulator.
+    for (; kb + S <= unmasked && kb + S < n_pad; kb += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        compute(kb + i, t[i], std::false_type{});
+        load(kb + i + S, t[i]);
+      }
+    }
     for (; kb + S < n_pad; kb += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
-        if (kb + i < unmasked) {
-          compute(kb + i, t[i], std::false_type{});
-        } else {
-          compute(kb + i, t[i], std::true_type{});
-        }
+        compute(kb + i, t[i], std::true_type{});
         load(kb + i + S, t[i]);
       }
     }
@@ -266,13 +393,14 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
 template <typename T, int D, int G>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
   constexpr int CG = PrefillShape<D>::kGroups, S = PrefillShape<D>::kDepth, NW = kPrefillWaves;
+  constexpr bool PAIRS = PrefillShape<D>::kPairs;
   const int per_wg = NW * CG * (16 / G);
   PrefillParams q = p;
   q.chunks = (p.max_query_len + per_wg - 1) / per_wg;
   const int64_t items = static_cast<int64_t>(p.num_seqs) * q.chunks * p.num_kv_heads;
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S>), dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S, PAIRS>), dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
                      0, stream, q);
   return hipGetLastError();
 }
