@@ -79,6 +79,9 @@ CASES = {
     "fp16-g2-empty-seq": (4, 2, 64, 16, [40, 50, 60], [10, 0, 60], "fp16"),
     "bf16-bs512": (8, 2, 64, 512, [1100, 513, 40], [600, 513, 1], "bf16"),
     "fp16-d128-bs1024": (16, 2, 128, 1024, [2100, 1025], [1100, 17], "fp16"),
+    # head_dim 64 at G = 1 and 8 (the paired-sub-tile path at every group size)
+    "bf16-d64-mha": (8, 8, 64, 16, [333, 47, 32], [333, 20, 31], "bf16"),
+    "fp16-d64-g8": (16, 2, 64, 32, [515, 96, 48], [200, 96, 33], "fp16"),
 }
 
 
