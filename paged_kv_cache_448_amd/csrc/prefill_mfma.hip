@@ -22,8 +22,8 @@
 //   O^T[D x 16 cols]      += V^T . P^T  (D/16 mfma 16x16x16 per group)
 //
 // At head_dim 64 the sub-tiles go in pairs, and P.V takes both at once: D/16
-// mfma 16x16x32 over 32 keys per group (half the matrix-core time of the
-// 16x16x16 products).
+// mfma 16x16x32 over 32 keys per group (on gfx950 one 16x16x32 product keeps
+// the matrix core as long as one 16x16x16, so this halves P.V's share).
 //
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
 // as in decode; the running reference is moved only when a score exceeds it by
@@ -32,8 +32,9 @@
 // shift); each lane tests its own scores against the matching threshold in
 // score units and the column maxima are folded across lanes only when a test
 // fires.  A key is visible to a column when it is not after the column's
-// position; sub-tiles entirely before the wave's first position need no mask.  Every wave sees every key its columns need, so nothing is combined
-// across waves: each lane divides and stores its columns' outputs itself.
+// position; sub-tiles entirely before the wave's first position need no mask.
+// Every wave sees every key its columns need, so nothing is combined across
+// waves: each lane divides and stores its columns' outputs itself.
 //
 // Work items: (sequence, kv head, chunk of NW * CG * 16/G new tokens), the
 // chunks of a sequence in descending order so the long causal rows start
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   };
 
   // P.V over a pair of key sub-tiles (32 keys) in one 16x16x32 product per 16
-  // dims, which the matrix cores run at twice the rate of two 16x16x16 ones.
+  // dims instead of two 16x16x16 ones.
   // Lane group kg holds keys 4kg..4kg+3 of the first sub-tile and then
   // 4kg..4kg+3 of the second: the order of the keys inside one product is
   // free as long as the V and P operands agree.  Both sub-tiles' scores share
