@@ -121,6 +121,15 @@ __device__ __forceinline__ void append_tokens_fp8(const DecodeParams& p) {
   }
 }
 
+// Headroom of each wave's lazily moved softmax reference, log2 units: the
+// reference moves only when a score exceeds it by more than this, so the
+// probabilities stay below 2^8 (within range of both 16-bit types) and most
+// steps need neither the column maximum across lanes nor a rescale (softmax
+// does not depend on the reference).  Measured on the Llama-3.2-1B batch over
+// FP8 pools: 18.6-18.7 us per step against 19.0 with the exact running
+// maximum.
+constexpr float kLazySlack = 8.f;
+
 template <int D> struct Fp8Tile {
   u32x2 k[D / 32];
   VCodes<D> v[4];
@@ -271,18 +280,18 @@ __global__ __launch_bounds__(NW * kWave, MINW) void decode_fp8_kernel(DecodePara
     float x[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) x[i] = 4 * kg + i < nvalid ? sc[i] * p.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    bm = max_xor32(max_xor16(bm));
-    const float mn = fmaxf(m, bm);
-    const float al = fast_exp2(m - mn);
-    m = mn;
-    const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - mn), fast_exp2(x[1] - mn));
-    const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - mn), fast_exp2(x[3] - mn));
-    l = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l * al));
-    if (__builtin_amdgcn_ballot_w64(al != 1.f)) {
+    const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(lm > m + kLazySlack)) {
+      const float mn = fmaxf(m, max_xor32(max_xor16(lm)));
+      const float al = fast_exp2(m - mn);
+      m = mn;
+      l *= al;
 #pragma unroll
       for (int j = 0; j < JV; ++j) o[j] *= al;
     }
+    const uint32_t p01 = Mma<T>::pack(fast_exp2(x[0] - m), fast_exp2(x[1] - m));
+    const uint32_t p23 = Mma<T>::pack(fast_exp2(x[2] - m), fast_exp2(x[3] - m));
+    l = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l));
     if (nvalid < 16) {
       const uint32_t m0 = (4 * kg < nvalid ? 0xffffu : 0u) | (4 * kg + 1 < nvalid ? 0xffff0000u : 0u);
       const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
