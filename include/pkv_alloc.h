@@ -80,9 +80,16 @@ int pkv_alloc_share_prefix(pkv_alloc* a, int64_t dst_seq, int64_t src_seq, int32
  * *cached_tokens_out receives the number of leading tokens (a multiple of
  * block_size) whose K/V those shared blocks already hold: the caller writes K/V
  * only for the tokens after them.  The new sequence's own full blocks are
- * registered for later prompts; a block leaves the registry when its last
- * holder frees it.  Only prompt blocks are registered (tokens appended later
- * are not known here).  PKV_E_NULL, PKV_E_EXISTS, PKV_E_NOMEM, PKV_E_SHAPE. */
+ * registered for later prompts.  A registered block outlives its holders: when
+ * the last one frees it, it keeps its K/V and stays findable (the page's case
+ * is a long system prompt that later requests repeat, so the cache should not
+ * depend on the requests overlapping in time) until the pool needs it -- free
+ * blocks holding nothing registered are handed out first, registered free
+ * blocks only when no other block is free, least recently freed first, and
+ * such a block leaves the registry when it is handed out.  So a match may
+ * also take free blocks out of the pool.  Only prompt blocks are registered
+ * (tokens appended later are not known here).  PKV_E_NULL, PKV_E_EXISTS,
+ * PKV_E_NOMEM, PKV_E_SHAPE. */
 int pkv_alloc_add_seq_prefix(pkv_alloc* a, int64_t seq_id, const int32_t* token_ids, int32_t num_tokens,
                              int32_t* cached_tokens_out);
 
@@ -105,8 +112,11 @@ int pkv_alloc_free_seq(pkv_alloc* a, int64_t seq_id);
 int pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
                            int32_t pad_value, int32_t* tables_out, int32_t* context_lens_out);
 
-/* Number of free blocks; number of live sequences; a sequence's token count. */
+/* Number of free blocks (including the registered ones below); number of free
+ * blocks that still hold a registered prompt block (prefix cache entries no
+ * live sequence holds); number of live sequences; a sequence's token count. */
 int32_t pkv_alloc_num_free(const pkv_alloc* a);
+int32_t pkv_alloc_num_cached(const pkv_alloc* a);
 int32_t pkv_alloc_num_seqs(const pkv_alloc* a);
 int pkv_alloc_context_len(const pkv_alloc* a, int64_t seq_id, int32_t* len_out);
 /* Reference count of a physical block (0 = free); -1 for an id outside the pool. */

@@ -57,6 +57,7 @@ PROTOTYPES = {
     "pkv_alloc_free_seq": (_c.c_int, [_vp, _i64]),
     "pkv_alloc_block_tables": (_c.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "pkv_alloc_num_free": (_i32, [_vp]),
+    "pkv_alloc_num_cached": (_i32, [_vp]),
     "pkv_alloc_num_seqs": (_i32, [_vp]),
     "pkv_alloc_context_len": (_c.c_int, [_vp, _i64, _vp]),
     "pkv_alloc_refcount": (_i32, [_vp, _i32]),

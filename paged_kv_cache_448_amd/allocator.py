@@ -44,9 +44,10 @@ class BlockAllocator:
         check(lib().pkv_alloc_share_prefix(self._h, int(dst_seq), int(src_seq), int(num_full_blocks)))
 
     def add_seq_prefix(self, seq_id: int, token_ids) -> int:
-        """Register seq_id with its prompt's token ids, sharing the leading full blocks a live
-        sequence already holds for the same tokens; returns how many leading tokens' K/V are
-        already in the pool (the caller writes K/V only for the rest)."""
+        """Register seq_id with its prompt's token ids, sharing the leading full blocks that
+        the pool still holds for the same tokens (held by a live sequence, or freed but not yet
+        reused); returns how many leading tokens' K/V are already in the pool (the caller
+        writes K/V only for the rest)."""
         ids = np.ascontiguousarray(token_ids, dtype=np.int32)
         out = ctypes.c_int32()
         check(lib().pkv_alloc_add_seq_prefix(self._h, int(seq_id), ids.ctypes.data if len(ids) else None, len(ids),
@@ -78,6 +79,11 @@ class BlockAllocator:
     @property
     def num_free(self) -> int:
         return int(lib().pkv_alloc_num_free(self._h))
+
+    @property
+    def num_cached(self) -> int:
+        """Free blocks that still hold a registered prompt block (counted in num_free too)."""
+        return int(lib().pkv_alloc_num_cached(self._h))
 
     @property
     def num_seqs(self) -> int:

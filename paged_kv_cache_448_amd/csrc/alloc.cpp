@@ -13,9 +13,12 @@
 // Prefix caching: a full prompt block is registered under a hash chained over
 // its tokens and every earlier block's, so a later prompt that starts with the
 // same full blocks of tokens finds them and shares them.  A match is confirmed
-// exactly (same tokens, same parent block), so a hash collision can never
-// share the wrong block.  A block leaves the registry when its last holder
-// frees it.
+// exactly (same tokens, same parent block in the same incarnation), so a hash
+// collision can never share the wrong block.  A registered block whose last
+// holder frees it keeps its K/V and stays findable: free blocks that hold
+// nothing registered are handed out first, and registered ones only when no
+// other block is free, least recently freed first (the block is then dropped
+// from the registry before it is reused).
 #include "pkv_alloc.h"
 
 #include <algorithm>
@@ -30,30 +33,73 @@ struct pkv_alloc {
   };
   int32_t num_blocks = 0;
   int32_t block_size = 0;
-  std::vector<int32_t> free_stack;  // next block handed out is free_stack.back()
+  // free blocks holding nothing registered; the next one handed out is
+  // free_stack.back()
+  std::vector<int32_t> free_stack;
+  // free blocks still registered (their K/V still findable), least recently
+  // freed at lru_head: a doubly linked list through lru_prev / lru_next (-1 ends)
+  std::vector<int32_t> lru_prev, lru_next;
+  int32_t lru_head = -1, lru_tail = -1, lru_size = 0;
   std::vector<int32_t> refcount;
   std::unordered_map<int64_t, Seq> seqs;
   // prefix registry: chained hash -> block; per block its hash (0: not
-  // registered), parent block (-1: first block of a prompt) and tokens
+  // registered), parent block (-1: first block of a prompt), the parent's
+  // incarnation when the block was registered, and tokens.  incarnation[b]
+  // grows each time b is handed out, so a registered child whose parent block
+  // was reused for other tokens can never be matched through it.
   std::unordered_map<uint64_t, int32_t> by_hash;
   std::vector<uint64_t> block_hash;
   std::vector<int32_t> block_parent;
+  std::vector<uint32_t> parent_incarnation;
+  std::vector<uint32_t> incarnation;
   std::vector<int32_t> block_tokens;
 
+  int32_t num_free() const { return static_cast<int32_t>(free_stack.size()) + lru_size; }
+  void lru_push(int32_t b) {
+    lru_prev[b] = lru_tail;
+    lru_next[b] = -1;
+    (lru_tail >= 0 ? lru_next[lru_tail] : lru_head) = b;
+    lru_tail = b;
+    ++lru_size;
+  }
+  void lru_remove(int32_t b) {
+    (lru_prev[b] >= 0 ? lru_next[lru_prev[b]] : lru_head) = lru_next[b];
+    (lru_next[b] >= 0 ? lru_prev[lru_next[b]] : lru_tail) = lru_prev[b];
+    lru_prev[b] = lru_next[b] = -1;
+    --lru_size;
+  }
+  void unregister(int32_t b) {
+    if (block_hash[b] == 0) return;
+    auto it = by_hash.find(block_hash[b]);
+    if (it != by_hash.end() && it->second == b) by_hash.erase(it);
+    block_hash[b] = 0;
+  }
+  // A free block for new contents: an unregistered one if any, else the least
+  // recently freed registered one, dropped from the registry.
   int32_t take() {
-    const int32_t b = free_stack.back();
-    free_stack.pop_back();
+    int32_t b;
+    if (!free_stack.empty()) {
+      b = free_stack.back();
+      free_stack.pop_back();
+    } else {
+      b = lru_head;
+      lru_remove(b);
+      unregister(b);
+    }
+    ++incarnation[b];
     refcount[b] = 1;
     return b;
   }
+  // One more holder of block b, which may be a free registered block.
+  void hold(int32_t b) {
+    if (refcount[b]++ == 0) lru_remove(b);
+  }
   void release(int32_t b) {
     if (--refcount[b] == 0) {
-      if (block_hash[b] != 0) {
-        auto it = by_hash.find(block_hash[b]);
-        if (it != by_hash.end() && it->second == b) by_hash.erase(it);
-        block_hash[b] = 0;
-      }
-      free_stack.push_back(b);
+      if (block_hash[b] != 0)
+        lru_push(b);
+      else
+        free_stack.push_back(b);
     }
   }
   int32_t blocks_for(int64_t tokens) const {
@@ -85,7 +131,12 @@ uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int32_t n) {
     }
   }
   uint64_t s = h;
-  const uint64_t z = splitmix64(s);
+  uint64_t z = splitmix64(s);
+#ifdef PKV_ALLOC_HASH_BITS
+  // test builds only: a hash of a few bits, so that collisions are common and
+  // the exact confirmation of every match is what keeps sharing correct
+  z &= (uint64_t{1} << PKV_ALLOC_HASH_BITS) - 1;
+#endif
   return z == 0 ? 1 : z;
 }
 
@@ -101,8 +152,12 @@ pkv_alloc* pkv_alloc_create(int32_t num_blocks, int32_t block_size, uint64_t shu
     a->num_blocks = num_blocks;
     a->block_size = block_size;
     a->refcount.assign(num_blocks, 0);
+    a->lru_prev.assign(num_blocks, -1);
+    a->lru_next.assign(num_blocks, -1);
     a->block_hash.assign(num_blocks, 0);
     a->block_parent.assign(num_blocks, -1);
+    a->parent_incarnation.assign(num_blocks, 0);
+    a->incarnation.assign(num_blocks, 0);
     // hand-out order: order[0] first
     std::vector<int32_t> order(num_blocks);
     for (int32_t i = 0; i < num_blocks; ++i) order[i] = i;
@@ -128,7 +183,7 @@ int pkv_alloc_add_seq(pkv_alloc* a, int64_t seq_id, int32_t num_tokens) {
   if (num_tokens < 0) return PKV_E_SHAPE;
   if (a->seqs.count(seq_id)) return PKV_E_EXISTS;
   const int32_t need = a->blocks_for(num_tokens);
-  if (need > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  if (need > a->num_free()) return PKV_E_NOMEM;
   pkv_alloc::Seq s;
   s.len = num_tokens;
   s.blocks.reserve(need);
@@ -148,7 +203,7 @@ int pkv_alloc_add_seq_shared(pkv_alloc* a, int64_t seq_id, int32_t num_tokens, i
   if (shared_tokens > num_tokens || shared_tokens > it->second.len) return PKV_E_SHAPE;
   const int32_t need = a->blocks_for(num_tokens);
   const int32_t fresh = need - num_shared_blocks;
-  if (fresh > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  if (fresh > a->num_free()) return PKV_E_NOMEM;
   pkv_alloc::Seq s;
   s.len = num_tokens;
   s.blocks.reserve(need);
@@ -190,43 +245,63 @@ int pkv_alloc_add_seq_prefix(pkv_alloc* a, int64_t seq_id, const int32_t* token_
   if (a->seqs.count(seq_id)) return PKV_E_EXISTS;
   const int32_t bs = a->block_size;
   const int32_t need = a->blocks_for(num_tokens), full = num_tokens / bs;
-  // longest run of leading full blocks already registered (exact match)
+  // longest run of leading full blocks already registered (exact match), live
+  // or free; the free ones matched leave the free pool
   std::vector<uint64_t> hashes(full);
-  int32_t shared = 0, parent = -1;
+  int32_t shared = 0, parent = -1, revived = 0;
   uint64_t h = 0x6a09e667f3bcc909ull;
   for (int32_t j = 0; j < full; ++j) {
     h = chain_hash(h, token_ids + static_cast<int64_t>(j) * bs, bs);
     hashes[j] = h;
     if (shared == j) {
       auto it = a->by_hash.find(h);
-      if (it != a->by_hash.end() && a->block_parent[it->second] == parent &&
-          std::equal(token_ids + static_cast<int64_t>(j) * bs, token_ids + static_cast<int64_t>(j + 1) * bs,
-                     a->block_tokens.begin() + static_cast<int64_t>(it->second) * bs)) {
-        parent = it->second;
-        ++shared;
+      if (it != a->by_hash.end()) {
+        const int32_t c = it->second;
+        if (a->block_parent[c] == parent &&
+            (parent < 0 || a->parent_incarnation[c] == a->incarnation[parent]) &&
+            std::equal(token_ids + static_cast<int64_t>(j) * bs, token_ids + static_cast<int64_t>(j + 1) * bs,
+                       a->block_tokens.begin() + static_cast<int64_t>(c) * bs)) {
+          parent = c;
+          ++shared;
+          revived += a->refcount[c] == 0;
+        }
       }
     }
   }
-  if (need - shared > static_cast<int32_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  if (need - shared > a->num_free() - revived) return PKV_E_NOMEM;
   try {
     if (a->block_tokens.empty()) a->block_tokens.assign(static_cast<size_t>(a->num_blocks) * bs, 0);
     pkv_alloc::Seq s;
     s.len = num_tokens;
     s.blocks.reserve(need);
     parent = -1;
+    // the shared blocks first, so that taking the fresh ones cannot reuse them
     for (int32_t j = 0; j < need; ++j) {
       int32_t b;
       if (j < shared) {
         b = a->by_hash.find(hashes[j])->second;
-        ++a->refcount[b];
+        a->hold(b);
       } else {
         b = a->take();
-        if (j < full && a->by_hash.find(hashes[j]) == a->by_hash.end()) {
-          // register the new full block (a block already registered under this
-          // hash stays the one later prompts find)
+        if (j < full) {
+          // register the new full block.  A block registered under the same
+          // hash could not be matched (the chained hash fixes every earlier
+          // token, so only a block whose ancestors are gone, or a collision,
+          // stops the match before it): it leaves the registry, and if free it
+          // holds nothing findable any more
+          auto it = a->by_hash.find(hashes[j]);
+          if (it != a->by_hash.end()) {
+            const int32_t e = it->second;
+            a->unregister(e);
+            if (a->refcount[e] == 0) {
+              a->lru_remove(e);
+              a->free_stack.push_back(e);
+            }
+          }
           a->by_hash.emplace(hashes[j], b);
           a->block_hash[b] = hashes[j];
           a->block_parent[b] = parent;
+          a->parent_incarnation[b] = parent >= 0 ? a->incarnation[parent] : 0;
           std::copy(token_ids + static_cast<int64_t>(j) * bs, token_ids + static_cast<int64_t>(j + 1) * bs,
                     a->block_tokens.begin() + static_cast<int64_t>(b) * bs);
         }
@@ -260,7 +335,7 @@ int pkv_alloc_append_slots(pkv_alloc* a, const int64_t* seq_ids, int32_t n, int6
       if (ss[k] == ss[i]) return PKV_E_SHAPE;  // one token per sequence per call
     if (ss[i]->len == static_cast<int64_t>(ss[i]->blocks.size()) * a->block_size) ++fresh;
   }
-  if (fresh > static_cast<int64_t>(a->free_stack.size())) return PKV_E_NOMEM;
+  if (fresh > a->num_free()) return PKV_E_NOMEM;
   for (int32_t i = 0; i < n; ++i) {
     pkv_alloc::Seq& s = *ss[i];
     const int32_t pos = s.len;
@@ -302,8 +377,10 @@ int pkv_alloc_block_tables(const pkv_alloc* a, const int64_t* seq_ids, int32_t n
 }
 
 int32_t pkv_alloc_num_free(const pkv_alloc* a) {
-  return a ? static_cast<int32_t>(a->free_stack.size()) : 0;
+  return a ? a->num_free() : 0;
 }
+
+int32_t pkv_alloc_num_cached(const pkv_alloc* a) { return a ? a->lru_size : 0; }
 
 int32_t pkv_alloc_num_seqs(const pkv_alloc* a) {
   return a ? static_cast<int32_t>(a->seqs.size()) : 0;

@@ -5,7 +5,11 @@ Pinned against a brute-force reading of the page's rule ("Nano-vLLM로 배우는
 are found by hash and reused): a new prompt shares exactly as many leading full
 blocks as the longest full-block prefix it has in common with the prompt of a
 live sequence -- a model that never hashes anything -- and the tables stay valid
-(oracle.alloc_check, shared blocks declared).
+(oracle.alloc_check, shared blocks declared).  Blocks whose holders have all
+finished stay cached until the pool reuses them (least recently freed first,
+after every block that holds nothing cached); under that pressure a model of
+what each physical block holds checks that a match only ever shares a block
+that still holds the new prompt's tokens.
 """
 import numpy as np
 import pytest
@@ -63,17 +67,76 @@ def test_partial_blocks_are_never_shared_and_appends_go_to_fresh_blocks():
     assert t3[0, 2] not in set(t[0, :2].tolist())
 
 
-def test_registry_follows_the_holders():
+def test_freed_prompt_blocks_stay_cached():
     a = pkv.BlockAllocator(32, BS)
     a.add_seq_prefix(0, _blocks(1, 2))
     a.add_seq_prefix(1, _blocks(1, 3))        # shares block "1", registers its own "3"
-    a.free_seq(0)                             # "1" still held by sequence 1; "2" is gone
-    assert a.add_seq_prefix(2, _blocks(1, 2)) == BS
+    t0, _ = a.block_tables([0], 2, pad_value=-1)
+    a.free_seq(0)                             # "1" still held by sequence 1; "2" is free but cached
+    assert a.num_free == 32 - 3 + 1 and a.num_cached == 1 and a.refcount(int(t0[0, 1])) == 0
+    assert a.add_seq_prefix(2, _blocks(1, 2)) == 2 * BS      # "2" comes back out of the free pool
+    t2, _ = a.block_tables([2], 2, pad_value=-1)
+    assert list(t2[0]) == list(t0[0]) and a.num_cached == 0 and a.num_free == 32 - 3
     assert a.add_seq_prefix(3, _blocks(1, 3)) == 2 * BS
     for s in (1, 2, 3):
         a.free_seq(s)
-    assert a.num_free == 32
-    assert a.add_seq_prefix(4, _blocks(1, 3)) == 0          # nothing live holds those tokens any more
+    assert a.num_free == 32 and a.num_cached == 3
+    assert a.add_seq_prefix(4, _blocks(1, 3)) == 2 * BS      # no holder left, the blocks still hold them
+    assert a.add_seq_prefix(5, _blocks(2)) == 0               # block "2" alone is another prefix
+
+
+def test_cached_blocks_are_reused_last_least_recently_freed_first():
+    a = pkv.BlockAllocator(8, BS)
+    a.add_seq_prefix(0, _blocks(1, 2, 3))
+    old, _ = a.block_tables([0], 3, pad_value=-1)
+    a.free_seq(0)                             # released last block first: "3", "2", "1" in that order
+    assert a.num_cached == 3 and a.num_free == 8
+    a.add_seq(1, 5 * BS)                      # the five blocks that hold nothing cached
+    t1, _ = a.block_tables([1], 5, pad_value=-1)
+    assert not set(t1[0].tolist()) & set(old[0].tolist()) and a.num_cached == 3
+    a.add_seq(2, BS)                          # the pool must reuse a cached block: "3", freed first
+    t2, _ = a.block_tables([2], 1, pad_value=-1)
+    assert t2[0, 0] == old[0, 2] and a.num_cached == 2
+    with pytest.raises(pkv.PkvError):         # "1" and "2" would come back; "3" needs a block
+        a.add_seq_prefix(3, _blocks(1, 2, 3))
+    assert a.num_cached == 2 and a.num_free == 2 and a.num_seqs == 2
+    a.free_seq(2)                             # an uncached block again
+    assert a.add_seq_prefix(3, _blocks(1, 2, 3)) == 2 * BS
+    t3, _ = a.block_tables([3], 3, pad_value=-1)
+    assert list(t3[0, :2]) == list(old[0, :2]) and t3[0, 2] == old[0, 2]
+    assert a.num_free == 0 and a.num_cached == 0
+
+
+def test_a_reused_parent_cuts_its_children_off():
+    """A registered block is matched only through the same incarnation of its parent
+    block: once the parent's id has been handed out again, the child's K/V may have
+    been computed after other tokens (the chained hash tells them apart only up to a
+    collision), so a match never reaches it, even when the id holds the same tokens
+    again; the new chain's own block takes its place in the registry."""
+    a = pkv.BlockAllocator(6, BS)
+    a.add_seq_prefix(0, _blocks(1, 2))            # b1, b2
+    a.add_seq_prefix(5, _blocks(3, 2))            # b3 and its own "2" (another chain)
+    a.add_seq(9, 2 * BS)                          # x1, x2: the pool is full
+    t0, _ = a.block_tables([0], 2, pad_value=-1)
+    b1, b2 = int(t0[0, 0]), int(t0[0, 1])
+    a.share_prefix(9, 0, 2)                       # 9 holds b1, b2; x1, x2 back in the pool
+    a.share_prefix(9, 5, 1)                       # 9 holds b3, b2: b2 without its parent
+    a.free_seq(0)                                 # b1 cached, b2 still held by 9
+    assert a.num_cached == 1 and a.refcount(b1) == 0 and a.refcount(b2) == 1
+    a.add_seq(7, 2 * BS)                          # x2, x1
+    a.add_seq(8, BS)                              # no uncached block left: b1 is reused
+    t8, _ = a.block_tables([8], 1, pad_value=-1)
+    assert int(t8[0, 0]) == b1 and a.num_cached == 0
+    a.free_seq(7)
+    a.free_seq(8)                                 # b1 on top of the free blocks
+    assert a.add_seq_prefix(4, _blocks(1, 2)) == 0   # "1" is gone, so nothing after it counts
+    t4, _ = a.block_tables([4], 2, pad_value=-1)
+    assert int(t4[0, 0]) == b1 and int(t4[0, 1]) != b2  # the same id holds "1" again, a new incarnation
+    assert a.add_seq_prefix(6, _blocks(1, 2)) == 2 * BS  # b1, then 4's "2", not b2
+    t6, _ = a.block_tables([6], 2, pad_value=-1)
+    assert list(t6[0]) == list(t4[0]) and a.refcount(b2) == 1
+    a.free_seq(9)                                 # b2 is no longer registered: an uncached free block
+    assert a.refcount(b2) == 0 and a.num_cached == 0     # (b3 is still held by 5)
 
 
 def test_nomem_changes_nothing():
@@ -95,17 +158,39 @@ def _common_full_blocks(p, q):
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_matches_brute_force_model(seed):
-    """Random admissions and frees over prompts built from a small alphabet of blocks."""
+    """Random admissions and frees over prompts built from a small alphabet of blocks,
+    with plain sequences competing for a small pool.  A prompt shares at least the
+    longest full-block prefix it has in common with a live sequence's prompt, and every
+    block it shares holds exactly its tokens up to that block's end (a per-block record
+    of contents, no hashing)."""
     rng = np.random.default_rng(seed)
-    N = 400
+    N = 120
     a = pkv.BlockAllocator(N, BS, shuffle_seed=seed + 1)
-    live = {}
+    live = {}          # prefix-admitted sequence -> prompt
+    plain = set()      # sequences registered by length only
+    held = {}          # physical block -> token prefix its K/V stands for (None: unknown)
     next_id = 0
-    for _ in range(300):
-        if live and rng.random() < 0.35:
-            sid = int(rng.choice(list(live)))
+    from_free = 0
+    for _ in range(600):
+        r = rng.random()
+        if (live or plain) and r < 0.3:
+            sid = int(rng.choice(list(live) + list(plain)))
             a.free_seq(sid)
-            del live[sid]
+            live.pop(sid, None)
+            plain.discard(sid)
+            continue
+        free_before = {b for b in range(N) if a.refcount(b) == 0}
+        if r < 0.45:
+            try:
+                a.add_seq(next_id, int(rng.integers(1, 6 * BS)))
+            except pkv.PkvError:
+                continue
+            t, lens = a.block_tables([next_id], N, pad_value=-1)
+            for b in t[0, :-(-int(lens[0]) // BS)]:
+                assert int(b) in free_before
+                held[int(b)] = None
+            plain.add(next_id)
+            next_id += 1
             continue
         names = [int(x) for x in rng.integers(0, 3, size=rng.integers(0, 6))]
         p = _blocks(*names, tail=int(rng.integers(0, BS)))
@@ -114,14 +199,24 @@ def test_matches_brute_force_model(seed):
             got = a.add_seq_prefix(next_id, p)
         except pkv.PkvError:
             continue
-        assert got == want * BS, (got, want)
+        assert got % BS == 0 and got >= want * BS, (got, want)
+        t, _ = a.block_tables([next_id], N, pad_value=-1)
+        for j in range(-(-len(p) // BS)):
+            b = int(t[0, j])
+            chain = tuple(p[:(j + 1) * BS].tolist())
+            if j < got // BS:
+                assert held.get(b) == chain, (j, b)
+                from_free += b in free_before
+            else:
+                assert b in free_before
+                held[b] = chain if (j + 1) * BS <= len(p) else None
         live[next_id] = p
         next_id += 1
-        ids = sorted(live)
-        if ids:
-            M = max(1, max(-(-len(live[i]) // BS) for i in ids))
-            t, lens = a.block_tables(ids, M, pad_value=-1)
-            used = [int(b) for i in range(len(ids)) for b in t[i, :-(-int(lens[i]) // BS)]]
-            shared = {b for b in used if used.count(b) > 1}
-            alloc_check.check_tables(t, lens, num_blocks=N, block_size=BS, pad_value=-1, shared=shared, appended=False)
-            assert a.num_free == N - len(set(used))
+        ids = sorted(live) + sorted(plain)
+        M = max(1, max(-(-a.context_len(i) // BS) for i in ids))
+        t, lens = a.block_tables(ids, M, pad_value=-1)
+        used = [int(b) for i in range(len(ids)) for b in t[i, :-(-int(lens[i]) // BS)]]
+        shared = {b for b in used if used.count(b) > 1}
+        alloc_check.check_tables(t, lens, num_blocks=N, block_size=BS, pad_value=-1, shared=shared, appended=False)
+        assert a.num_free == N - len(set(used)) and 0 <= a.num_cached <= a.num_free
+    assert from_free > 0, "some matches should have taken cached blocks back out of the free pool"
