@@ -171,6 +171,50 @@ def test_large_block_sizes(Hq, Hkv, D, bs, dtype):
             print(f"bs {bs} G {Hq // Hkv} D {D} impl {impl} partition {pt}: max|err| {e:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,bs,dtype,longest", [(32, 8, 64, 16, "bf16", 131072),
+                                                       (16, 2, 128, 256, "fp16", 65536)])
+def test_very_long_context(Hq, Hkv, D, bs, dtype, longest):
+    """One context at the long end of what such a model serves (128k tokens; 64k at
+    head_dim 128) beside short ones: the automatic split gives tens of partitions
+    per row for the merge to fold (and the largest workspace of these tests); the
+    forced 8192-token partitions (the most one workgroup takes) and the host
+    dispatch order must agree with the oracle too."""
+    lens = [longest, 1, 17, 5000]
+    wl, kc, vc, dw, d = _custom(Hq, Hkv, D, bs, lens, dtype, seed=longest % 97)
+    ref = oracle_decode(wl, 0, kc, vc)
+    order = torch.from_numpy(pkv.decode_schedule(lens)).cuda()
+    impls = [i for i in ("simt", "mfma") if pkv.decode_supported(i, dtype, D, Hq // Hkv)]
+    assert impls
+    for impl in impls:
+        for pt in (0, 8192):
+            out = gpu_decode(wl, dw, d, impl=impl, partition_tokens=pt)
+            r, e = assert_parity(to_bits(out), ref, dtype, f"L {longest} impl {impl} partition {pt}")
+            print(f"L {longest} G {Hq // Hkv} D {D} impl {impl} partition {pt}: max|err| {e:.2e} "
+                  f"(ratio {r:.3f})", flush=True)
+    c = wl.cfg
+    out = pkv.paged_attn_decode(d.q, d.k_cache, d.v_cache, dw.tables, dw.lens, c.scale, max_context_len=longest,
+                                seq_order=order)
+    assert_parity(to_bits(out), ref, dtype, f"L {longest} dispatch order")
+
+
+def test_large_batch():
+    """4,096 sequences of 1-300 tokens: 32,768 (sequence, kv head) workgroups in one
+    launch, in sequence order and in the host dispatch order."""
+    rng = np.random.default_rng(4096)
+    lens = rng.integers(1, 301, size=4096).tolist()
+    wl, kc, vc, dw, d = _custom(32, 8, 64, 16, lens, "bf16", seed=4096)
+    ref = oracle_decode(wl, 0, kc, vc)
+    c = wl.cfg
+    order = torch.from_numpy(pkv.decode_schedule(lens)).cuda()
+    for impl in [i for i in ("simt", "mfma") if pkv.decode_supported(i, "bf16", 64, 4)]:
+        out = gpu_decode(wl, dw, d, impl=impl)
+        assert_parity(to_bits(out), ref, "bf16", f"B 4096 impl {impl}")
+    out = pkv.paged_attn_decode(d.q, d.k_cache, d.v_cache, dw.tables, dw.lens, c.scale, max_context_len=300,
+                                seq_order=order)
+    r, e = assert_parity(to_bits(out), ref, "bf16", "B 4096 dispatch order")
+    print(f"B 4096: max|err| {e:.2e} (ratio {r:.3f})", flush=True)
+
+
 def test_length_one_is_exactly_v0():
     lens = [1] * 9
     wl, kc, vc, dw, d = _custom(8, 2, 64, 16, lens, seed=3)
