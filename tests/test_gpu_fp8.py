@@ -115,10 +115,12 @@ _WORKLOADS = {
     "bf16-g16-bs256": lambda: workloads.custom(16, 1, 64, 256, [5000, 31, 2600], "bf16", seed=6),
     "bf16-bs512": lambda: workloads.custom(8, 2, 64, 512, [1, 511, 513, 1025, 2049], "bf16", seed=7),
     "fp16-d128-bs1024": lambda: workloads.custom(16, 2, 128, 1024, [17, 1023, 1025, 3000], "fp16", seed=8),
+    # a 64k-token context beside short ones: tens of partitions per row for the merge
+    "bf16-long-64k": lambda: workloads.custom(32, 8, 64, 16, [65536, 1, 17, 5000], "bf16", seed=9),
 }
 PARTS = {"tiny": [0, 16, 32], "llama3.2-1b-b64": [0, 4096, 128, 512], "fp16-d128-g8-ragged": [0, 2112, 256, 512],
          "fp16-d128-mha": [0, 128], "bf16-g16-bs256": [0, 8192, 256, 1024], "bf16-bs512": [0, 512, 1024],
-         "fp16-d128-bs1024": [0, 1024, 256]}
+         "fp16-d128-bs1024": [0, 1024, 256], "bf16-long-64k": [0, 8192]}
 
 
 def _device_pools(key):
@@ -196,7 +198,8 @@ def test_fp8_rejects_bad_scales_and_dtypes():
 
 
 FUSED_PARTS = {"tiny": [0, 16], "llama3.2-1b-b64": [0, 512], "fp16-d128-g8-ragged": [0, 256],
-               "bf16-g16-bs256": [0, 1024], "bf16-bs512": [0, 512], "fp16-d128-bs1024": [0, 1024]}
+               "bf16-g16-bs256": [0, 1024], "bf16-bs512": [0, 512], "fp16-d128-bs1024": [0, 1024],
+               "bf16-long-64k": [0]}
 
 
 def _poisoned_fused_pools(key, slots):

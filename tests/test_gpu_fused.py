@@ -104,6 +104,30 @@ def test_fused_large_block_sizes(Hq, Hkv, D, bs, dtype):
         print(f"bs {bs} partition {pt}: fused == two calls, max|err| {e:.2e}", flush=True)
 
 
+def test_fused_very_long_context():
+    """Fused == two calls, and within tolerance of the oracle, with a 131,072-token
+    context beside short ones (the automatic split: tens of partitions per row) and
+    in the host dispatch order."""
+    lens = [131072, 1, 17, 5000]
+    wl = _custom(lens, Hq=32, Hkv=8, D=64, bs=16, dtype="bf16", seed=131)
+    kc_ref, vc_ref = oracle_caches(wl, 0)
+    ref = oracle_decode(wl, 0, kc_ref, vc_ref)
+    order = torch.from_numpy(pkv.decode_schedule(lens)).cuda()
+    dwa, da = _fresh(wl, 0)
+    out_a = to_bits(_two_calls(wl, dwa, da))
+    for seq_order in (None, order):
+        dwb, db = _fresh(wl, 0)
+        _poison_slots(wl, dwb, db, dwb.slots)
+        out_b = to_bits(pkv.append_paged_attn_decode(db.q, db.k_new, db.v_new, dwb.slots, db.k_cache, db.v_cache,
+                                                     dwb.tables, dwb.lens, wl.cfg.scale, max_context_len=131072,
+                                                     seq_order=seq_order))
+        assert np.array_equal(to_bits(db.k_cache).ravel(), kc_ref) and np.array_equal(to_bits(db.v_cache).ravel(),
+                                                                                         vc_ref), "pools"
+        assert np.array_equal(out_a, out_b), f"order {seq_order is not None}: output differs from two calls"
+        r, e = assert_parity(out_b, ref, "bf16", "L 131072 fused")
+        print(f"L 131072 fused (order {seq_order is not None}) == two calls, max|err| {e:.2e}", flush=True)
+
+
 def test_fused_length_one_is_exactly_v_new():
     """With L = 1 the appended token is the whole context: out = v_new exactly."""
     wl = _custom([1] * 7, Hq=8, Hkv=2)

@@ -164,3 +164,28 @@ def test_prefill_parity_benchmark_batch_sampled():
                         num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads, block_size=c.block_size)
     r, e = assert_parity(got[rows], ref, c.dtype, "benchmark batch, sampled rows")
     print(f"benchmark batch: {len(rows)} sampled rows, max|err| {e:.2e} (ratio {r:.3f})", flush=True)
+
+
+def test_prefill_long_prompt_sampled():
+    """A 32,768-token context whose last 16,384 tokens are new (the first half a cached
+    prefix) beside a short prompt, at the benchmark's shape: sampled rows (first, last,
+    the rows at every 4,096th new token and random ones) against the decode oracle over
+    p + 1 positions."""
+    lens, new = [32768, 40], [16384, 40]
+    wl, q, k_new, v_new, qs, slots = _setup(32, 8, 64, 16, lens, new, "bf16", seed=32768)
+    kc, vc = _oracle_pools(wl, k_new, v_new, slots)
+    c = wl.cfg
+    got = _gpu(wl, q, k_new, v_new, qs, slots, max(new))
+    rng = np.random.default_rng(5)
+    rows, seq, ctx = [], [], []
+    for i, (L, n) in enumerate(zip(lens, new)):
+        js = {0, n - 1, *range(0, n, 4096), *(int(x) for x in rng.integers(0, n, size=6))}
+        for j in sorted(js):
+            rows.append(qs[i] + j)
+            seq.append(i)
+            ctx.append(L - n + j + 1)  # new token j is position L - n + j
+    rows = np.array(rows)
+    ref = oracle.decode(q[rows], kc, vc, wl.block_tables[seq], np.array(ctx), c.scale, dtype=c.dtype,
+                        num_blocks=wl.num_blocks, num_kv_heads=c.num_kv_heads, block_size=c.block_size)
+    r, e = assert_parity(got[rows], ref, c.dtype, "long prompt, sampled rows")
+    print(f"long prompt: {len(rows)} sampled rows, max|err| {e:.2e} (ratio {r:.3f})", flush=True)
