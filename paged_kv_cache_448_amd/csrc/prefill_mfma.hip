@@ -186,8 +186,9 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     u32x2 vop[JV];
 #pragma unroll
     for (int j = 0; j < JV; ++j) vop[j] = v_operand<D>(t.v, j);
-    if (key0 + 16 > L) {
-      // keys past the context (the last block's tail) may hold anything: zero their V
+    if (decltype(causal)::value && key0 + 16 > L) {
+      // keys past the context (the last block's tail) may hold anything: zero
+      // their V (only a masked sub-tile can reach past the context)
       const int nvalid = L - key0;
       const uint32_t m0 = (4 * kg < nvalid ? 0xffffu : 0u) | (4 * kg + 1 < nvalid ? 0xffff0000u : 0u);
       const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
@@ -249,8 +250,10 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
         va[j] = v_operand<D>(ta.v, j);
         vb[j] = v_operand<D>(tb.v, j);
       }
-      if (key0 + 32 > L) {
-        // keys past the context (the last block's tail) may hold anything: zero their V
+      if (decltype(causal)::value && key0 + 32 > L) {
+        // keys past the context (the last block's tail) may hold anything: zero
+        // their V.  Only a masked pair can reach past the context: every key of
+        // an unmasked one precedes the wave's first position
         const int na = L - key0, nb = L - key0 - 16;
         const uint32_t a0 = (4 * kg < na ? 0xffffu : 0u) | (4 * kg + 1 < na ? 0xffff0000u : 0u);
         const uint32_t a1 = (4 * kg + 2 < na ? 0xffffu : 0u) | (4 * kg + 3 < na ? 0xffff0000u : 0u);
@@ -274,28 +277,38 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
       for (int j = 0; j < JK; ++j) sa = Mma<T>::qk(ta.k[j], qop[cg][j], sa);
 #pragma unroll
       for (int j = 0; j < JK; ++j) sb = Mma<T>::qk(tb.k[j], qop[cg][j], sb);
-      float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
-      if constexpr (decltype(causal)::value) {
+      const float x[8] = {sa[0], sa[1], sa[2], sa[3], sb[0], sb[1], sb[2], sb[3]};
+      bool vis[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = key0 + (i >> 2) * 16 + 4 * kg + (i & 3) <= pos[cg] ? x[i] : -INFINITY;
-      }
-      const float lm = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-      if (__builtin_amdgcn_ballot_w64(lm > thr[cg])) {
-        const float bm = max_xor32(max_xor16(lm)) * sc2;
+      for (int i = 0; i < 8; ++i)
+        vis[i] = !decltype(causal)::value || key0 + (i >> 2) * 16 + 4 * kg + (i & 3) <= pos[cg];
+      // exponents against the current reference, log2 units (masked keys -inf);
+      // their maximum needs no quieting of the products' NaNs first, as a
+      // maximum of raw scores would
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = vis[i] ? fmaf(x[i], sc2, -m[cg]) : -INFINITY;
+      const float lm = fmaxf(fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3])), fmaxf(fmaxf(y[4], y[5]), fmaxf(y[6], y[7])));
+      if (__builtin_amdgcn_ballot_w64(lm > kRescaleSlack)) {
+        // the column maxima of the raw scores (the exponents are +inf while
+        // the reference is still -inf)
+        float xm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xm = fmaxf(xm, vis[i] ? x[i] : -INFINITY);
+        const float bm = max_xor32(max_xor16(xm)) * sc2;
         const bool up = bm > m[cg] + kRescaleSlack;
         const float mn = up ? bm : m[cg];
         const float al = fast_exp2(m[cg] - mn);
         m[cg] = mn;
-        thr[cg] = (mn + kRescaleSlack) / sc2;
         l[cg] *= al;
 #pragma unroll
         for (int j = 0; j < JV; ++j) o[cg][j] *= al;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = vis[i] ? fmaf(x[i], sc2, -mn) : -INFINITY;
       }
-      const float nm = -m[cg];
       uint32_t pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pw[i] = Mma<T>::pack(fast_exp2(fmaf(x[2 * i], sc2, nm)), fast_exp2(fmaf(x[2 * i + 1], sc2, nm)));
+      for (int i = 0; i < 4; ++i) pw[i] = Mma<T>::pack(fast_exp2(y[2 * i]), fast_exp2(y[2 * i + 1]));
       l[cg] = Mma<T>::sum2(pw[3], Mma<T>::sum2(pw[2], Mma<T>::sum2(pw[1], Mma<T>::sum2(pw[0], l[cg]))));
       const u32x4 pop = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
