@@ -29,9 +29,9 @@
 // as in decode; the running reference is moved only when a score exceeds it by
 // more than a fixed slack, so most sub-tiles need no rescaling of the
 // accumulators (the result is the same: softmax does not depend on the
-// shift); each lane tests its own scores against the matching threshold in
-// score units and the column maxima are folded across lanes only when a test
-// fires.  A key is visible to a column when it is not after the column's
+// shift); each lane computes its scores' exponents against the current
+// reference and tests their maximum against the slack, and the column maxima
+// are folded across lanes only when a test fires.  A key is visible to a column when it is not after the column's
 // position; sub-tiles entirely before the wave's first position need no mask.
 // Every wave sees every key its columns need, so nothing is combined across
 // waves: each lane divides and stores its columns' outputs itself.
@@ -116,8 +116,8 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   const int nsub = (p0 + last_tok + 1 + 15) >> 4;
   const int unmasked = (p0 + first + 1) >> 4;    // sub-tiles before this are visible to every column
 
-  // the scale is positive (checked by the caller), so a score above a
-  // threshold is a probability above the threshold's
+  // the scale is positive (checked by the caller), so a column's largest
+  // score gives its largest exponent
   const float sc2 = p.scale_log2;  // softmax scale * log2(e)
   int pos[CG];
   u32x4 qop[CG][JK];
@@ -167,14 +167,12 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
   };
 
-  // thr: the score above which a probability would exceed 2^kRescaleSlack,
-  // (m + kRescaleSlack) / scale in score units
-  float m[CG], l[CG], thr[CG];
+  // per column: softmax reference m (log2 units, scale folded in), denominator l
+  float m[CG], l[CG];
   f32x4 o[CG][JV];
 #pragma unroll
   for (int cg = 0; cg < CG; ++cg) {
     m[cg] = -INFINITY;
-    thr[cg] = -INFINITY;
     l[cg] = 0.f;
 #pragma unroll
     for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -198,35 +196,59 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
         vop[j].y &= m1;
       }
     }
+    // every column group's q.K first, so that the products of one group run
+    // while the next one's are issued (the rescale test below is a branch the
+    // scheduler does not move work across)
+    f32x4 sc[CG];
 #pragma unroll
     for (int cg = 0; cg < CG; ++cg) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      sc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < JK; ++j) sc = Mma<T>::qk(t.k[j], qop[cg][j], sc);
-      float x[4] = {sc[0], sc[1], sc[2], sc[3]};
-      if constexpr (decltype(causal)::value) {
+      for (int j = 0; j < JK; ++j) sc[cg] = Mma<T>::qk(t.k[j], qop[cg][j], sc[cg]);
+    }
+    // exponents against each column's reference, log2 units (masked keys -inf)
+    bool vis[CG][4];
+    float y[CG][4], lm[CG];
+    bool any = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = key0 + 4 * kg + i <= pos[cg] ? x[i] : -INFINITY;
+    for (int cg = 0; cg < CG; ++cg) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vis[cg][i] = !decltype(causal)::value || key0 + 4 * kg + i <= pos[cg];
+        y[cg][i] = vis[cg][i] ? fmaf(sc[cg][i], sc2, -m[cg]) : -INFINITY;
       }
-      // lazy rescaling: the reference m moves only when a score exceeds it by
-      // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack;
-      // each lane compares its own scores with the threshold, the column
-      // maxima are folded across lanes only when one exceeds it
-      if (__builtin_amdgcn_ballot_w64(x[0] > thr[cg] || x[1] > thr[cg] || x[2] > thr[cg] || x[3] > thr[cg])) {
-        const float lm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-        const float bm = max_xor32(max_xor16(lm)) * sc2;
+      lm[cg] = fmaxf(fmaxf(y[cg][0], y[cg][1]), fmaxf(y[cg][2], y[cg][3]));
+      any |= lm[cg] > kRescaleSlack;
+    }
+    // lazy rescaling: the reference m moves only when a score exceeds it by
+    // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack;
+    // each lane tests its own scores, the column maxima are folded across
+    // lanes only when one exceeds it
+    if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+      for (int cg = 0; cg < CG; ++cg) {
+        if (!__builtin_amdgcn_ballot_w64(lm[cg] > kRescaleSlack)) continue;
+        // the column maxima of the raw scores (the exponents are +inf while
+        // the reference is still -inf)
+        float xm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xm = fmaxf(xm, vis[cg][i] ? sc[cg][i] : -INFINITY);
+        const float bm = max_xor32(max_xor16(xm)) * sc2;
         const bool up = bm > m[cg] + kRescaleSlack;
         const float mn = up ? bm : m[cg];
         const float al = fast_exp2(m[cg] - mn);
         m[cg] = mn;
-        thr[cg] = (mn + kRescaleSlack) / sc2;
         l[cg] *= al;
 #pragma unroll
         for (int j = 0; j < JV; ++j) o[cg][j] *= al;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[cg][i] = vis[cg][i] ? fmaf(sc[cg][i], sc2, -mn) : -INFINITY;
       }
-      const float nm = -m[cg];
-      const uint32_t p01 = Mma<T>::pack(fast_exp2(fmaf(x[0], sc2, nm)), fast_exp2(fmaf(x[1], sc2, nm)));
-      const uint32_t p23 = Mma<T>::pack(fast_exp2(fmaf(x[2], sc2, nm)), fast_exp2(fmaf(x[3], sc2, nm)));
+    }
+#pragma unroll
+    for (int cg = 0; cg < CG; ++cg) {
+      const uint32_t p01 = Mma<T>::pack(fast_exp2(y[cg][0]), fast_exp2(y[cg][1]));
+      const uint32_t p23 = Mma<T>::pack(fast_exp2(y[cg][2]), fast_exp2(y[cg][3]));
       l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg]));
       const u32x2 pop = {p01, p23};
 #pragma unroll
