@@ -59,17 +59,19 @@ constexpr float kRescaleSlack = 8.f;
 template <int D> struct PrefillShape;
 template <> struct PrefillShape<64> {
   static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = true;
+  static constexpr bool kPairs = true, kShared = false;
 };
 template <> struct PrefillShape<128> {
   static constexpr int kGroups = 2, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = false;
+  static constexpr bool kPairs = false, kShared = true;
 };
 
 constexpr int kPrefillWaves = 4;
 
-template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS>
+template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
+  static_assert(!SHARED || (D == 128 && !PAIRS && NW * kWave == 16 * D / 8),
+                "shared sub-tiles: one 16-byte chunk of K and of V per thread");
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -87,7 +89,11 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   const int s0 = p.query_start[seq];
   const int n = p.query_start[seq + 1] - s0;
   const int first = (chunk * NW + wv) * QPW;  // index of the wave's first new token
-  if (s0 < 0 || n <= 0 || s0 + n > p.num_tokens || first >= n) return;
+  const int first_wg = chunk * NW * QPW;       // the workgroup's
+  // with shared sub-tiles every wave of a live workgroup takes part in the
+  // loads and barriers; a wave past the last new token computes nothing
+  if (s0 < 0 || n <= 0 || s0 + n > p.num_tokens || (SHARED ? first_wg : first) >= n) return;
+  const bool idle = first >= n;
   const int L = p.context_lens[seq];
 
   // column (cg, r): new token first + cg*QPC + r/G, q head kvh*G + r%G
@@ -113,7 +119,11 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
 
   const int p0 = L - n;                          // position of new token 0
   const int last_tok = min(first + QPW, n) - 1;  // the wave's last new token
-  const int nsub = (p0 + last_tok + 1 + 15) >> 4;
+  const int nsub = idle ? 0 : (p0 + last_tok + 1 + 15) >> 4;
+  // sub-tiles the workgroup reads (its last wave's), and those all its waves see whole
+  const int nsub_wg = (p0 + min(first_wg + NW * QPW, n) + 15) >> 4;
+  const int unmasked_wg = (p0 + first_wg + 1) >> 4;
+  const int nfetch = SHARED ? nsub_wg : nsub;
   const int unmasked = (p0 + first + 1) >> 4;    // sub-tiles before this are visible to every column
 
   // the scale is positive (checked by the caller), so a column's largest
@@ -136,7 +146,7 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   auto fetch_window = [&](int base) {
     const int k = base + lane;
     tid = 0;
-    if (k < nsub) {
+    if (k < nfetch) {
       const int tok0 = 16 * k;
       const int blk = tok0 / p.block_size;
       const int phys = p.block_tables[static_cast<size_t>(seq) * p.max_blocks_per_seq + blk];
@@ -338,7 +348,73 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     }
   };
 
-  if constexpr (PAIRS) {
+  if constexpr (SHARED) {
+    // The workgroup's waves read the same sub-tiles, so each is loaded once:
+    // thread i fetches 16-byte chunk i of the sub-tile's K and of its V (the
+    // 4 KB of each are contiguous in the pool) two sub-tiles ahead into
+    // registers and stores them to one of two LDS slots; every wave then reads
+    // its K operands and V row slices from LDS.  One workgroup barrier per
+    // sub-tile orders the stores of one slot against the reads of the other.
+    // Chunk c of row w sits at chunk (c ^ w) of the row, so that the 16 lanes
+    // reading one operand (16 rows, or 16 chunks of one row) hit distinct banks.
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    __shared__ __align__(16) u32x4 kv_lds[2][2][16 * CPR];  // [slot][K, V][chunk]
+    const int tix = threadIdx.x;
+    const int crow = tix / CPR;
+    const int cst = crow * CPR + ((tix % CPR) ^ crow);
+    const int last_wg = nsub_wg - 1;
+    u32x4 sk[2], sv[2];
+    auto gload = [&](int k, u32x4& a, u32x4& b) {
+      const int kk = min(k, last_wg);
+      if ((kk & ~63) != win) fetch_window(kk & ~63);
+      int sub = __builtin_amdgcn_readlane(tid, kk & 63);
+      bad |= sub < 0 && kk < nsub;  // only the sub-tiles this wave attends to
+      sub = max(sub, 0);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(p.k_cache + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(p.v_cache + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
+      a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * tix, 0, 0));
+      b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * tix, 0, 0));
+    };
+    auto lstore = [&](int slot, const u32x4& a, const u32x4& b) {
+      kv_lds[slot][0][cst] = a;
+      kv_lds[slot][1][cst] = b;
+    };
+    auto lread = [&](int slot, Tile<D>& t) {
+#pragma unroll
+      for (int j = 0; j < JK; ++j) t.k[j] = kv_lds[slot][0][r * CPR + ((kg + 4 * j) ^ r)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t.v[i].w = kv_lds[slot][1][(4 * kg + i) * CPR + (r ^ (4 * kg + i))];
+    };
+    // step k: sub-tile k from slot k & 1; the loads of k + 2 go out first and
+    // sub-tile k + 1 (loaded a step earlier) is stored to the other slot last
+    auto step = [&](int k, int slot, auto causal) {
+      gload(k + 2, sk[slot], sv[slot]);
+      if (k < nsub) {
+        Tile<D> t;
+        lread(slot, t);
+        compute(k, t, causal);
+      }
+      lstore(slot ^ 1, sk[slot ^ 1], sv[slot ^ 1]);
+      __syncthreads();
+    };
+    gload(0, sk[0], sv[0]);
+    gload(1, sk[1], sv[1]);
+    lstore(0, sk[0], sv[0]);
+    __syncthreads();
+    int k = 0;
+    // steps every wave sees whole, then the rest with the causal mask (the
+    // loop bounds are the workgroup's, so every wave meets every barrier)
+    for (; k + 2 <= unmasked_wg && k + 2 <= nsub_wg; k += 2) {
+      step(k, 0, std::false_type{});
+      step(k + 1, 1, std::false_type{});
+    }
+    for (; k < nsub_wg; k += 2) {
+      step(k, 0, std::true_type{});
+      if (k + 1 < nsub_wg) step(k + 1, 1, std::true_type{});
+    }
+  } else if constexpr (PAIRS) {
     // S pairs in flight.  Pair q is sub-tiles 2q and 2q+1; a pair with a
     // masked sub-tile runs the causal variant, so does the last pair when it
     // has a single sub-tile (its second one, past the wave's last position,
@@ -436,7 +512,8 @@ hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
   const int64_t items = static_cast<int64_t>(p.num_seqs) * q.chunks * p.num_kv_heads;
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S, PAIRS>), dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S, PAIRS, PrefillShape<D>::kShared>),
+                     dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
                      0, stream, q);
   return hipGetLastError();
 }

@@ -99,24 +99,39 @@ def test_prefill_parity(name):
         print(f"{name} max_query_len {mql}: max|err| {e:.2e} (ratio {r:.3f})", flush=True)
 
 
-def test_prefill_invalid_sequences_give_nan_only_in_their_rows():
-    Hq, Hkv, D, bs, lens, new, dtype = CASES["tiny"]
+@pytest.mark.parametrize("name", ["tiny", "fp16-d128-g8"])
+def test_prefill_invalid_sequences_give_nan_only_in_their_rows(name):
+    Hq, Hkv, D, bs, lens, new, dtype = CASES[name]
     wl, q, k_new, v_new, qs, slots = _setup(Hq, Hkv, D, bs, lens, new, dtype, seed=3)
     kc, vc = _oracle_pools(wl, k_new, v_new, slots)
     c = wl.cfg
     ref = oracle_prefill(q, kc, vc, wl.block_tables, wl.context_lens, qs, c.scale, dtype=dtype,
                          num_blocks=wl.num_blocks, num_kv_heads=Hkv, block_size=bs)
     from oracle.numerics import bits_to_f64
+    n0 = new[0]
     lens = wl.context_lens.copy()
-    lens[0] = 3  # fewer context positions than new tokens
+    lens[0] = n0 - 2  # fewer context positions than new tokens
     got = _gpu(wl, q, k_new, v_new, qs, slots, max(new), lens=lens)
-    assert np.all(np.isnan(bits_to_f64(got[:5], dtype)))
-    assert_parity(got[5:], ref[5:], dtype, "valid sequence next to an invalid one")
+    assert np.all(np.isnan(bits_to_f64(got[:n0], dtype)))
+    assert_parity(got[n0:], ref[n0:], dtype, "valid sequence next to an invalid one")
     tables = wl.block_tables.copy()
     tables[1, 0] = wl.num_blocks  # first block of sequence 1 outside the pool
     got = _gpu(wl, q, k_new, v_new, qs, slots, max(new), tables=tables)
-    assert np.all(np.isnan(bits_to_f64(got[5:], dtype)))
-    assert_parity(got[:5], ref[:5], dtype, "valid sequence next to a bad block id")
+    assert np.all(np.isnan(bits_to_f64(got[n0:], dtype)))
+    assert_parity(got[:n0], ref[:n0], dtype, "valid sequence next to a bad block id")
+    if wl.context_lens[0] > 2 * wl.cfg.block_size:
+        # a block id outside the pool late in sequence 0: the rows that attend to it are NaN,
+        # the earlier rows (whose positions come before it) are not
+        tables = wl.block_tables.copy()
+        blk = (int(wl.context_lens[0]) - 1) // wl.cfg.block_size
+        tables[0, blk] = -1
+        got = _gpu(wl, q, k_new, v_new, qs, slots, max(new), tables=tables)
+        first_pos = int(wl.context_lens[0]) - n0
+        cut = blk * wl.cfg.block_size - first_pos  # new tokens before this index precede the bad block
+        rows = bits_to_f64(got[:n0], dtype)
+        assert np.all(np.isnan(rows[cut:])), "rows attending to the bad block must be NaN"
+        assert_parity(got[:max(cut, 0)], ref[:max(cut, 0)], dtype, "rows before a late bad block")
+        assert_parity(got[n0:], ref[n0:], dtype, "sequence next to a late bad block")
 
 
 def test_prefill_rejects_bad_arguments():
