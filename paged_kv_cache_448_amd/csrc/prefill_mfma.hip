@@ -59,7 +59,7 @@ constexpr float kRescaleSlack = 8.f;
 template <int D> struct PrefillShape;
 template <> struct PrefillShape<64> {
   static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = true, kShared = false;
+  static constexpr bool kPairs = true, kShared = true;
 };
 template <> struct PrefillShape<128> {
   static constexpr int kGroups = 2, kDepth = 2, kBlocksPerCu = 2;
@@ -70,8 +70,8 @@ constexpr int kPrefillWaves = 4;
 
 template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
-  static_assert(!SHARED || (D == 128 && !PAIRS && NW * kWave == 16 * D / 8),
-                "shared sub-tiles: one 16-byte chunk of K and of V per thread");
+  static_assert(!SHARED || (NW * kWave == 256 && ((D == 128 && !PAIRS) || (D == 64 && PAIRS))),
+                "shared sub-tiles: two 16-byte chunks of a step's K and V per thread");
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -348,7 +348,72 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     }
   };
 
-  if constexpr (SHARED) {
+  if constexpr (SHARED && PAIRS) {
+    // As below (head_dim 128), one step per pair of sub-tiles: the pair's K
+    // and V (2 KB each per sub-tile) come in as 512 chunks of 16 bytes, the
+    // first two waves fetching K and the other two V, chunk t & 127 of each
+    // sub-tile.  Rows are 8 chunks here, so chunk c of row w sits at chunk
+    // c ^ ((w >> 1) & 7): the 16 lanes reading one K operand (rows 0..15)
+    // and those reading one V row (8 bytes each) still hit distinct banks.
+    constexpr int CPR = D / 8;                                  // 8
+    __shared__ __align__(16) u32x4 kv_lds[2][2][2][16 * CPR];  // [slot][sub-tile][K, V][chunk]
+    const int tix = threadIdx.x;
+    const int half = wv >> 1;  // 0: K, 1: V (wave-uniform)
+    const int u = tix & 127, crow = u / CPR;
+    const int cst = crow * CPR + ((u % CPR) ^ ((crow >> 1) & 7));
+    const int last_wg = nsub_wg - 1;
+    const int npair_wg = (nsub_wg + 1) >> 1, upair_wg = unmasked_wg >> 1, npair = (nsub + 1) >> 1;
+    const uint16_t* pool = half ? p.v_cache : p.k_cache;
+    u32x4 sa[2], sb[2];  // staging: [slot] sub-tile 2q, 2q + 1
+    auto gsub = [&](int k) {
+      const int kk = min(k, last_wg);
+      if ((kk & ~63) != win) fetch_window(kk & ~63);
+      int sub = __builtin_amdgcn_readlane(tid, kk & 63);
+      bad |= sub < 0 && kk < nsub;  // only the sub-tiles this wave attends to
+      sub = max(sub, 0);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(pool + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
+      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * u, 0, 0));
+    };
+    auto lread = [&](int slot, int h, Tile<D>& t) {
+#pragma unroll
+      for (int j = 0; j < JK; ++j) t.k[j] = kv_lds[slot][h][0][r * CPR + ((kg + 4 * j) ^ ((r >> 1) & 7))];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int w = 4 * kg + i;
+        t.v[i].w = reinterpret_cast<const u32x2*>(&kv_lds[slot][h][1][w * CPR + ((r >> 1) ^ ((w >> 1) & 7))])[r & 1];
+      }
+    };
+    auto step = [&](int q, int slot, auto causal) {
+      sa[slot] = gsub(2 * q + 4);
+      sb[slot] = gsub(2 * q + 5);
+      if (q < npair) {
+        Tile<D> ta, tb;
+        lread(slot, 0, ta);
+        lread(slot, 1, tb);
+        compute2(q, ta, tb, causal);
+      }
+      kv_lds[slot ^ 1][0][half][cst] = sa[slot ^ 1];
+      kv_lds[slot ^ 1][1][half][cst] = sb[slot ^ 1];
+      __syncthreads();
+    };
+    sa[0] = gsub(0);
+    sb[0] = gsub(1);
+    sa[1] = gsub(2);
+    sb[1] = gsub(3);
+    kv_lds[0][0][half][cst] = sa[0];
+    kv_lds[0][1][half][cst] = sb[0];
+    __syncthreads();
+    int q = 0;
+    for (; q + 2 <= upair_wg && q + 2 <= npair_wg; q += 2) {
+      step(q, 0, std::false_type{});
+      step(q + 1, 1, std::false_type{});
+    }
+    for (; q < npair_wg; q += 2) {
+      step(q, 0, std::true_type{});
+      if (q + 1 < npair_wg) step(q + 1, 1, std::true_type{});
+    }
+  } else if constexpr (SHARED) {
     // The workgroup's waves read the same sub-tiles, so each is loaded once:
     // thread i fetches 16-byte chunk i of the sub-tile's K and of its V (the
     // 4 KB of each are contiguous in the pool) two sub-tiles ahead into
