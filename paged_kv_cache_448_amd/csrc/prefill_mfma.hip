@@ -63,15 +63,15 @@ template <> struct PrefillShape<64> {
 };
 template <> struct PrefillShape<128> {
   static constexpr int kGroups = 2, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = false, kShared = true;
+  static constexpr bool kPairs = true, kShared = true;
 };
 
 constexpr int kPrefillWaves = 4;
 
 template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
-  static_assert(!SHARED || (NW * kWave == 256 && ((D == 128 && !PAIRS) || (D == 64 && PAIRS))),
-                "shared sub-tiles: two 16-byte chunks of a step's K and V per thread");
+  static_assert(!SHARED || (NW * kWave == 256 && (PAIRS || D == 128)),
+                "shared sub-tiles: whole 16-byte chunks of a step's K and V per thread");
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -349,62 +349,90 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   };
 
   if constexpr (SHARED && PAIRS) {
-    // As below (head_dim 128), one step per pair of sub-tiles: the pair's K
-    // and V (2 KB each per sub-tile) come in as 512 chunks of 16 bytes, the
-    // first two waves fetching K and the other two V, chunk t & 127 of each
-    // sub-tile.  Rows are 8 chunks here, so chunk c of row w sits at chunk
-    // c ^ ((w >> 1) & 7): the 16 lanes reading one K operand (rows 0..15)
-    // and those reading one V row (8 bytes each) still hit distinct banks.
-    constexpr int CPR = D / 8;                                  // 8
-    __shared__ __align__(16) u32x4 kv_lds[2][2][2][16 * CPR];  // [slot][sub-tile][K, V][chunk]
+    // As below for single sub-tiles, one step per pair of sub-tiles: the
+    // pair's K and V (16 rows of D/8 chunks of 16 bytes each, per sub-tile)
+    // come in as 64 * D/8 chunks, D/32 per thread, each load instruction
+    // covering one sub-tile's K or V (wave-uniform).  Chunk c of row w sits
+    // at chunk c ^ swz(w) of its row: with 16-chunk rows swz(w) = w, with
+    // 8-chunk rows (w >> 1) & 7, so that the 16 lanes reading one K operand
+    // (rows 0..15) and those reading one V row hit distinct banks.
+    constexpr int CPR = D / 8;                     // chunks per row
+    constexpr int CPT = 16 * CPR;                  // chunks of one sub-tile's K (or V)
+    constexpr int NL = 4 * CPT / (NW * kWave);     // loads per thread per step
+    __shared__ __align__(16) u32x4 kv_lds[2][2][2][CPT];  // [slot][sub-tile][K, V][chunk]
+    auto swz = [](int w) { return CPR == 16 ? w : (w >> 1) & 7; };
     const int tix = threadIdx.x;
-    const int half = wv >> 1;  // 0: K, 1: V (wave-uniform)
-    const int u = tix & 127, crow = u / CPR;
-    const int cst = crow * CPR + ((u % CPR) ^ ((crow >> 1) & 7));
     const int last_wg = nsub_wg - 1;
     const int npair_wg = (nsub_wg + 1) >> 1, upair_wg = unmasked_wg >> 1, npair = (nsub + 1) >> 1;
-    const uint16_t* pool = half ? p.v_cache : p.k_cache;
-    u32x4 sa[2], sb[2];  // staging: [slot] sub-tile 2q, 2q + 1
-    auto gsub = [&](int k) {
-      const int kk = min(k, last_wg);
-      if ((kk & ~63) != win) fetch_window(kk & ~63);
-      int sub = __builtin_amdgcn_readlane(tid, kk & 63);
-      bad |= sub < 0 && kk < nsub;  // only the sub-tiles this wave attends to
-      sub = max(sub, 0);
-      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(pool + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
-      return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * u, 0, 0));
+    // load e of this thread: chunk g = tix + 256 e of the pair, i.e. sub-tile
+    // g / (2 CPT), K or V (g / CPT) & 1, chunk u = g % CPT at row u / CPR
+    int cst[NL], hsub[NL], hkv[NL], goff[NL];
+#pragma unroll
+    for (int e = 0; e < NL; ++e) {
+      const int g = tix + NW * kWave * e;
+      hsub[e] = __builtin_amdgcn_readfirstlane(g / (2 * CPT));
+      hkv[e] = __builtin_amdgcn_readfirstlane((g / CPT) & 1);
+      const int u = g % CPT, w = u / CPR;
+      goff[e] = 16 * u;
+      cst[e] = w * CPR + ((u % CPR) ^ swz(w));
+    }
+    u32x4 stg[2][NL];  // [slot] staging
+    auto gload = [&](int q, u32x4 (&a)[NL]) {
+      int sub2[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = min(2 * q + h, last_wg);
+        if ((kk & ~63) != win) fetch_window(kk & ~63);
+        int sub = __builtin_amdgcn_readlane(tid, kk & 63);
+        bad |= sub < 0 && kk < nsub;  // only the sub-tiles this wave attends to
+        sub2[h] = max(sub, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < NL; ++e) {
+        const uint16_t* base = (hkv[e] ? p.v_cache : p.k_cache) + static_cast<size_t>(sub2[hsub[e]]) * (16 * D);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, -1,
+                                                                            kBufferConfig);
+        a[e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, goff[e], 0, 0));
+      }
+    };
+    auto lstore = [&](int slot, const u32x4 (&a)[NL]) {
+#pragma unroll
+      for (int e = 0; e < NL; ++e) kv_lds[slot][hsub[e]][hkv[e]][cst[e]] = a[e];
     };
     auto lread = [&](int slot, int h, Tile<D>& t) {
 #pragma unroll
-      for (int j = 0; j < JK; ++j) t.k[j] = kv_lds[slot][h][0][r * CPR + ((kg + 4 * j) ^ ((r >> 1) & 7))];
+      for (int j = 0; j < JK; ++j) t.k[j] = kv_lds[slot][h][0][r * CPR + ((kg + 4 * j) ^ swz(r))];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int w = 4 * kg + i;
-        t.v[i].w = reinterpret_cast<const u32x2*>(&kv_lds[slot][h][1][w * CPR + ((r >> 1) ^ ((w >> 1) & 7))])[r & 1];
+        if constexpr (D == 128) {
+          t.v[i].w = kv_lds[slot][h][1][w * CPR + (r ^ swz(w))];
+        } else {
+          // 8 bytes: half r & 1 of chunk r >> 1
+          t.v[i].w = reinterpret_cast<const u32x2*>(&kv_lds[slot][h][1][w * CPR + ((r >> 1) ^ swz(w))])[r & 1];
+        }
       }
     };
+    // step q: pair q from slot q & 1; the loads of pair q + 2 go out first and
+    // pair q + 1 (loaded a step earlier) is stored to the other slot last
     auto step = [&](int q, int slot, auto causal) {
-      sa[slot] = gsub(2 * q + 4);
-      sb[slot] = gsub(2 * q + 5);
+      gload(q + 2, stg[slot]);
       if (q < npair) {
         Tile<D> ta, tb;
         lread(slot, 0, ta);
         lread(slot, 1, tb);
         compute2(q, ta, tb, causal);
       }
-      kv_lds[slot ^ 1][0][half][cst] = sa[slot ^ 1];
-      kv_lds[slot ^ 1][1][half][cst] = sb[slot ^ 1];
+      lstore(slot ^ 1, stg[slot ^ 1]);
       __syncthreads();
     };
-    sa[0] = gsub(0);
-    sb[0] = gsub(1);
-    sa[1] = gsub(2);
-    sb[1] = gsub(3);
-    kv_lds[0][0][half][cst] = sa[0];
-    kv_lds[0][1][half][cst] = sb[0];
+    gload(0, stg[0]);
+    gload(1, stg[1]);
+    lstore(0, stg[0]);
     __syncthreads();
     int q = 0;
+    // pairs every wave sees whole, then the rest with the causal mask (the
+    // loop bounds are the workgroup's, so every wave meets every barrier)
     for (; q + 2 <= upair_wg && q + 2 <= npair_wg; q += 2) {
       step(q, 0, std::false_type{});
       step(q + 1, 1, std::false_type{});
