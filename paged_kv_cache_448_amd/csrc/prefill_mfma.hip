@@ -14,16 +14,19 @@
 // now (new-token position, q head) pairs: column c of a column group is q head
 // kvh*G + c % G of the group's position c / G, so a group covers 16 / G
 // positions.  A wave owns CG consecutive column groups and walks the key
-// sub-tiles (16 keys) from key 0 up to its last position, each sub-tile loaded
-// once (the decode kernel's buffer loads, S in flight) and used by all CG
-// groups:
+// sub-tiles (16 keys) from key 0 up to its last position, each sub-tile used
+// by all CG groups:
 //
 //   S^T[16 keys x 16 cols] = K . Q^T    (D/32 mfma 16x16x32 per group)
 //   O^T[D x 16 cols]      += V^T . P^T  (D/16 mfma 16x16x16 per group)
 //
-// At head_dim 64 the sub-tiles go in pairs, and P.V takes both at once: D/16
-// mfma 16x16x32 over 32 keys per group (on gfx950 one 16x16x32 product keeps
-// the matrix core as long as one 16x16x16, so this halves P.V's share).
+// The sub-tiles go in pairs, and P.V takes both at once: D/16 mfma 16x16x32
+// over 32 keys per group (on gfx950 one 16x16x32 product keeps the matrix core
+// as long as one 16x16x16, so this halves P.V's share).  The four waves of a
+// workgroup walk the same keys, so each pair is loaded once per workgroup,
+// through LDS (kShared; the per-wave register ring of the decode kernel's
+// buffer loads remains as the other path): with every wave loading its own,
+// the CUs' texture-address units were the bound.
 //
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
 // as in decode; the running reference is moved only when a score exceeds it by
@@ -31,8 +34,9 @@
 // accumulators (the result is the same: softmax does not depend on the
 // shift); each lane computes its scores' exponents against the current
 // reference and tests their maximum against the slack, and the column maxima
-// are folded across lanes only when a test fires.  A key is visible to a column when it is not after the column's
-// position; sub-tiles entirely before the wave's first position need no mask.
+// are folded across lanes only when a test fires.  A key is visible to a
+// column when it is not after the column's position; sub-tiles entirely
+// before the workgroup's first position need no mask.
 // Every wave sees every key its columns need, so nothing is combined across
 // waves: each lane divides and stores its columns' outputs itself.
 //
@@ -52,10 +56,11 @@ namespace {
 constexpr float kRescaleSlack = 8.f;
 
 // Column groups per wave (accumulators of 64 VGPRs at either head_dim), key
-// sub-tiles (kPairs: pairs of them) in flight per wave, and workgroups per CU.
-// Two workgroups of four waves give each wave 256 registers.  Measured on the
-// prompt batches: deeper rings, a third workgroup per CU (three column groups)
-// and pairs at head_dim 128 were no faster.
+// sub-tiles (kPairs: pairs of them) in flight per wave when each wave loads
+// its own, and workgroups per CU.  Two workgroups of four waves give each wave
+// 256 registers.  Measured on the prompt batches: a third workgroup per CU
+// (two or three column groups) was no faster, with or without the shared
+// sub-tiles.
 template <int D> struct PrefillShape;
 template <> struct PrefillShape<64> {
   static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2;
