@@ -75,8 +75,8 @@ constexpr int kPrefillWaves = 4;
 
 template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS, bool SHARED>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
-  static_assert(!SHARED || (NW * kWave == 256 && (PAIRS || D == 128)),
-                "shared sub-tiles: whole 16-byte chunks of a step's K and V per thread");
+  static_assert(!SHARED || (NW * kWave == 256 && PAIRS),
+                "shared sub-tiles: pairs, whole 16-byte chunks of a step's K and V per thread");
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -354,18 +354,23 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   };
 
   if constexpr (SHARED && PAIRS) {
-    // As below for single sub-tiles, one step per pair of sub-tiles: the
-    // pair's K and V (16 rows of D/8 chunks of 16 bytes each, per sub-tile)
-    // come in as 64 * D/8 chunks, D/32 per thread, each load instruction
-    // covering one sub-tile's K or V (wave-uniform).  Chunk c of row w sits
-    // at chunk c ^ swz(w) of its row: with 16-chunk rows swz(w) = w, with
-    // 8-chunk rows (w >> 1) & 7, so that the 16 lanes reading one K operand
-    // (rows 0..15) and those reading one V row hit distinct banks.
+    // The workgroup's waves read the same sub-tiles, so each pair is loaded
+    // once: its K and V (16 rows of D/8 chunks of 16 bytes each, per
+    // sub-tile, contiguous in the pool) come in as 64 * D/8 chunks, D/32 per
+    // thread, each load instruction covering one sub-tile's K or V
+    // (wave-uniform), two pairs ahead into registers, then stored to one of
+    // two LDS slots; every wave reads its K operands and V row slices from
+    // LDS.  One workgroup barrier per pair orders the stores of one slot
+    // against the reads of the other.  Chunk c of row w sits at chunk
+    // c ^ swz(w) of its row, swz taking bits of w that keep the reads of one
+    // operand (16 rows, or 16 lanes of one row) and the stores free of bank
+    // conflicts (measured: rocprofv3's SQ_LDS_BANK_CONFLICT reads 0 at both
+    // head_dims; swz(w) = w at head_dim 128 did not).
     constexpr int CPR = D / 8;                     // chunks per row
     constexpr int CPT = 16 * CPR;                  // chunks of one sub-tile's K (or V)
     constexpr int NL = 4 * CPT / (NW * kWave);     // loads per thread per step
     __shared__ __align__(16) u32x4 kv_lds[2][2][2][CPT];  // [slot][sub-tile][K, V][chunk]
-    auto swz = [](int w) { return CPR == 16 ? w : (w >> 1) & 7; };
+    auto swz = [](int w) { return CPR == 16 ? ((w >> 1) & 7) | ((w & 1) << 3) : (w >> 1) & 7; };
     const int tix = threadIdx.x;
     const int last_wg = nsub_wg - 1;
     const int npair_wg = (nsub_wg + 1) >> 1, upair_wg = unmasked_wg >> 1, npair = (nsub + 1) >> 1;
@@ -445,72 +450,6 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     for (; q < npair_wg; q += 2) {
       step(q, 0, std::true_type{});
       if (q + 1 < npair_wg) step(q + 1, 1, std::true_type{});
-    }
-  } else if constexpr (SHARED) {
-    // The workgroup's waves read the same sub-tiles, so each is loaded once:
-    // thread i fetches 16-byte chunk i of the sub-tile's K and of its V (the
-    // 4 KB of each are contiguous in the pool) two sub-tiles ahead into
-    // registers and stores them to one of two LDS slots; every wave then reads
-    // its K operands and V row slices from LDS.  One workgroup barrier per
-    // sub-tile orders the stores of one slot against the reads of the other.
-    // Chunk c of row w sits at chunk (c ^ w) of the row, so that the 16 lanes
-    // reading one operand (16 rows, or 16 chunks of one row) hit distinct banks.
-    constexpr int CPR = D / 8;  // 16-byte chunks per row
-    __shared__ __align__(16) u32x4 kv_lds[2][2][16 * CPR];  // [slot][K, V][chunk]
-    const int tix = threadIdx.x;
-    const int crow = tix / CPR;
-    const int cst = crow * CPR + ((tix % CPR) ^ crow);
-    const int last_wg = nsub_wg - 1;
-    u32x4 sk[2], sv[2];
-    auto gload = [&](int k, u32x4& a, u32x4& b) {
-      const int kk = min(k, last_wg);
-      if ((kk & ~63) != win) fetch_window(kk & ~63);
-      int sub = __builtin_amdgcn_readlane(tid, kk & 63);
-      bad |= sub < 0 && kk < nsub;  // only the sub-tiles this wave attends to
-      sub = max(sub, 0);
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(p.k_cache + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint16_t*>(p.v_cache + static_cast<size_t>(sub) * (16 * D)), 0, -1, kBufferConfig);
-      a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, 16 * tix, 0, 0));
-      b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, 16 * tix, 0, 0));
-    };
-    auto lstore = [&](int slot, const u32x4& a, const u32x4& b) {
-      kv_lds[slot][0][cst] = a;
-      kv_lds[slot][1][cst] = b;
-    };
-    auto lread = [&](int slot, Tile<D>& t) {
-#pragma unroll
-      for (int j = 0; j < JK; ++j) t.k[j] = kv_lds[slot][0][r * CPR + ((kg + 4 * j) ^ r)];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) t.v[i].w = kv_lds[slot][1][(4 * kg + i) * CPR + (r ^ (4 * kg + i))];
-    };
-    // step k: sub-tile k from slot k & 1; the loads of k + 2 go out first and
-    // sub-tile k + 1 (loaded a step earlier) is stored to the other slot last
-    auto step = [&](int k, int slot, auto causal) {
-      gload(k + 2, sk[slot], sv[slot]);
-      if (k < nsub) {
-        Tile<D> t;
-        lread(slot, t);
-        compute(k, t, causal);
-      }
-      lstore(slot ^ 1, sk[slot ^ 1], sv[slot ^ 1]);
-      __syncthreads();
-    };
-    gload(0, sk[0], sv[0]);
-    gload(1, sk[1], sv[1]);
-    lstore(0, sk[0], sv[0]);
-    __syncthreads();
-    int k = 0;
-    // steps every wave sees whole, then the rest with the causal mask (the
-    // loop bounds are the workgroup's, so every wave meets every barrier)
-    for (; k + 2 <= unmasked_wg && k + 2 <= nsub_wg; k += 2) {
-      step(k, 0, std::false_type{});
-      step(k + 1, 1, std::false_type{});
-    }
-    for (; k < nsub_wg; k += 2) {
-      step(k, 0, std::true_type{});
-      if (k + 1 < nsub_wg) step(k + 1, 1, std::true_type{});
     }
   } else if constexpr (PAIRS) {
     // S pairs in flight.  Pair q is sub-tiles 2q and 2q+1; a pair with a
