@@ -82,6 +82,9 @@ CASES = {
     # head_dim 64 at G = 1 and 8 (the paired-sub-tile path at every group size)
     "bf16-d64-mha": (8, 8, 64, 16, [333, 47, 32], [333, 20, 31], "bf16"),
     "fp16-d64-g8": (16, 2, 64, 32, [515, 96, 48], [200, 96, 33], "fp16"),
+    # head_dim 128 at G = 2 and 16 (the variants that spill a few registers, and the widest group)
+    "fp16-d128-g2": (8, 4, 128, 16, [300, 129, 17], [300, 1, 17], "fp16"),
+    "bf16-d128-g16": (16, 1, 128, 32, [700, 33], [400, 33], "bf16"),
 }
 
 
