@@ -24,9 +24,8 @@
 // over 32 keys per group (on gfx950 one 16x16x32 product keeps the matrix core
 // as long as one 16x16x16, so this halves P.V's share).  The four waves of a
 // workgroup walk the same keys, so each pair is loaded once per workgroup,
-// through LDS (kShared; the per-wave register ring of the decode kernel's
-// buffer loads remains as the other path): with every wave loading its own,
-// the CUs' texture-address units were the bound.
+// through LDS: with every wave loading its own (the decode kernel's per-wave
+// register ring), the CUs' texture-address units were the bound.
 //
 // Online softmax per column in fp32 (log2 domain), P rounded to the 16-bit type
 // as in decode; the running reference is moved only when a score exceeds it by
@@ -55,28 +54,24 @@ namespace {
 // to 2^8 before the reference catches up; exact in bf16 and fp16).
 constexpr float kRescaleSlack = 8.f;
 
-// Column groups per wave (accumulators of 64 VGPRs at either head_dim), key
-// sub-tiles (kPairs: pairs of them) in flight per wave when each wave loads
-// its own, and workgroups per CU.  Two workgroups of four waves give each wave
-// 256 registers.  Measured on the prompt batches: a third workgroup per CU
-// (two or three column groups) was no faster, with or without the shared
-// sub-tiles.
+// Column groups per wave (accumulators of 64 VGPRs at either head_dim) and
+// workgroups per CU.  Two workgroups of four waves give each wave 256
+// registers.  Measured on the prompt batches: a third workgroup per CU (two or
+// three column groups), one workgroup of eight waves, and two pairs per
+// barrier were no faster.
 template <int D> struct PrefillShape;
 template <> struct PrefillShape<64> {
-  static constexpr int kGroups = 4, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = true, kShared = true;
+  static constexpr int kGroups = 4, kBlocksPerCu = 2;
 };
 template <> struct PrefillShape<128> {
-  static constexpr int kGroups = 2, kDepth = 2, kBlocksPerCu = 2;
-  static constexpr bool kPairs = true, kShared = true;
+  static constexpr int kGroups = 2, kBlocksPerCu = 2;
 };
 
 constexpr int kPrefillWaves = 4;
 
-template <typename T, int D, int G, int NW, int CG, int S, bool PAIRS, bool SHARED>
+template <typename T, int D, int G, int NW, int CG>
 __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void prefill_mfma_kernel(PrefillParams p) {
-  static_assert(!SHARED || (NW * kWave == 256 && PAIRS),
-                "shared sub-tiles: pairs, whole 16-byte chunks of a step's K and V per thread");
+  static_assert(NW * kWave == 256, "shared sub-tiles: whole 16-byte chunks of a step's K and V per thread");
   constexpr int JK = D / 32, JV = D / 16;
   constexpr int QPC = 16 / G;       // positions per column group
   constexpr int QPW = CG * QPC;     // positions per wave
@@ -95,9 +90,9 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   const int n = p.query_start[seq + 1] - s0;
   const int first = (chunk * NW + wv) * QPW;  // index of the wave's first new token
   const int first_wg = chunk * NW * QPW;       // the workgroup's
-  // with shared sub-tiles every wave of a live workgroup takes part in the
-  // loads and barriers; a wave past the last new token computes nothing
-  if (s0 < 0 || n <= 0 || s0 + n > p.num_tokens || (SHARED ? first_wg : first) >= n) return;
+  // every wave of a live workgroup takes part in the loads and barriers; a
+  // wave past the last new token computes nothing
+  if (s0 < 0 || n <= 0 || s0 + n > p.num_tokens || first_wg >= n) return;
   const bool idle = first >= n;
   const int L = p.context_lens[seq];
 
@@ -128,8 +123,6 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   // sub-tiles the workgroup reads (its last wave's), and those all its waves see whole
   const int nsub_wg = (p0 + min(first_wg + NW * QPW, n) + 15) >> 4;
   const int unmasked_wg = (p0 + first_wg + 1) >> 4;
-  const int nfetch = SHARED ? nsub_wg : nsub;
-  const int unmasked = (p0 + first + 1) >> 4;    // sub-tiles before this are visible to every column
 
   // the scale is positive (checked by the caller), so a column's largest
   // score gives its largest exponent
@@ -151,7 +144,7 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
   auto fetch_window = [&](int base) {
     const int k = base + lane;
     tid = 0;
-    if (k < nfetch) {
+    if (k < nsub_wg) {
       const int tok0 = 16 * k;
       const int blk = tok0 / p.block_size;
       const int phys = p.block_tables[static_cast<size_t>(seq) * p.max_blocks_per_seq + blk];
@@ -160,26 +153,6 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
                 : -1;
     }
     win = base;
-  };
-
-  const int last = nsub - 1;
-  const int koff = (r * D + kg * 8) * 2;
-  const int voff = (4 * kg * D + r * JV) * 2;
-  auto load = [&](int k, Tile<D>& t) {
-    const int kk = min(k, last);
-    if ((kk & ~63) != win) fetch_window(kk & ~63);
-    int sub = __builtin_amdgcn_readlane(tid, kk & 63);
-    bad |= sub < 0;
-    sub = max(sub, 0);
-    const uint16_t* kt = p.k_cache + static_cast<size_t>(sub) * (16 * D);
-    const uint16_t* vt = p.v_cache + static_cast<size_t>(sub) * (16 * D);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kt), 0, -1, kBufferConfig);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vt), 0, -1, kBufferConfig);
-#pragma unroll
-    for (int j = 0; j < JK; ++j)
-      t.k[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 64 * j, 0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = VSlice<D>::load(rv, voff, i * D * 2);
   };
 
   // per column: softmax reference m (log2 units, scale folded in), denominator l
@@ -193,90 +166,13 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     for (int j = 0; j < JV; ++j) o[cg][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // causal: std::true_type for sub-tiles that some column must not fully see
-  auto compute = [&](int k, Tile<D>& t, auto causal) {
-    const int key0 = 16 * k;
-    u32x2 vop[JV];
-#pragma unroll
-    for (int j = 0; j < JV; ++j) vop[j] = v_operand<D>(t.v, j);
-    if (decltype(causal)::value && key0 + 16 > L) {
-      // keys past the context (the last block's tail) may hold anything: zero
-      // their V (only a masked sub-tile can reach past the context)
-      const int nvalid = L - key0;
-      const uint32_t m0 = (4 * kg < nvalid ? 0xffffu : 0u) | (4 * kg + 1 < nvalid ? 0xffff0000u : 0u);
-      const uint32_t m1 = (4 * kg + 2 < nvalid ? 0xffffu : 0u) | (4 * kg + 3 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-      for (int j = 0; j < JV; ++j) {
-        vop[j].x &= m0;
-        vop[j].y &= m1;
-      }
-    }
-    // every column group's q.K first, so that the products of one group run
-    // while the next one's are issued (the rescale test below is a branch the
-    // scheduler does not move work across)
-    f32x4 sc[CG];
-#pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
-      sc[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < JK; ++j) sc[cg] = Mma<T>::qk(t.k[j], qop[cg][j], sc[cg]);
-    }
-    // exponents against each column's reference, log2 units (masked keys -inf)
-    bool vis[CG][4];
-    float y[CG][4], lm[CG];
-    bool any = false;
-#pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vis[cg][i] = !decltype(causal)::value || key0 + 4 * kg + i <= pos[cg];
-        y[cg][i] = vis[cg][i] ? fmaf(sc[cg][i], sc2, -m[cg]) : -INFINITY;
-      }
-      lm[cg] = fmaxf(fmaxf(y[cg][0], y[cg][1]), fmaxf(y[cg][2], y[cg][3]));
-      any |= lm[cg] > kRescaleSlack;
-    }
-    // lazy rescaling: the reference m moves only when a score exceeds it by
-    // more than kRescaleSlack, so probabilities stay below 2^kRescaleSlack;
-    // each lane tests its own scores, the column maxima are folded across
-    // lanes only when one exceeds it
-    if (__builtin_amdgcn_ballot_w64(any)) {
-#pragma unroll
-      for (int cg = 0; cg < CG; ++cg) {
-        if (!__builtin_amdgcn_ballot_w64(lm[cg] > kRescaleSlack)) continue;
-        // the column maxima of the raw scores (the exponents are +inf while
-        // the reference is still -inf)
-        float xm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xm = fmaxf(xm, vis[cg][i] ? sc[cg][i] : -INFINITY);
-        const float bm = max_xor32(max_xor16(xm)) * sc2;
-        const bool up = bm > m[cg] + kRescaleSlack;
-        const float mn = up ? bm : m[cg];
-        const float al = fast_exp2(m[cg] - mn);
-        m[cg] = mn;
-        l[cg] *= al;
-#pragma unroll
-        for (int j = 0; j < JV; ++j) o[cg][j] *= al;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[cg][i] = vis[cg][i] ? fmaf(sc[cg][i], sc2, -mn) : -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int cg = 0; cg < CG; ++cg) {
-      const uint32_t p01 = Mma<T>::pack(fast_exp2(y[cg][0]), fast_exp2(y[cg][1]));
-      const uint32_t p23 = Mma<T>::pack(fast_exp2(y[cg][2]), fast_exp2(y[cg][3]));
-      l[cg] = Mma<T>::sum2(p23, Mma<T>::sum2(p01, l[cg]));
-      const u32x2 pop = {p01, p23};
-#pragma unroll
-      for (int j = 0; j < JV; ++j) o[cg][j] = Mma<T>::pv(vop[j], pop, o[cg][j]);
-    }
-  };
-
-  // P.V over a pair of key sub-tiles (32 keys) in one 16x16x32 product per 16
-  // dims instead of two 16x16x16 ones.
-  // Lane group kg holds keys 4kg..4kg+3 of the first sub-tile and then
-  // 4kg..4kg+3 of the second: the order of the keys inside one product is
-  // free as long as the V and P operands agree.  Both sub-tiles' scores share
-  // one softmax reference.
+  // One pair of key sub-tiles (32 keys): q.K per sub-tile, then P.V over both
+  // in one 16x16x32 product per 16 dims instead of two 16x16x16 ones.  Lane
+  // group kg holds keys 4kg..4kg+3 of the first sub-tile and then 4kg..4kg+3
+  // of the second: the order of the keys inside one product is free as long as
+  // the V and P operands agree.  Both sub-tiles' scores share one softmax
+  // reference.  causal: std::true_type for pairs that some column must not
+  // fully see.
   auto compute2 = [&](int q, Tile<D>& ta, Tile<D>& tb, auto causal) {
     const int key0 = 32 * q;
     u32x4 vop[JV];
@@ -353,7 +249,7 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
     }
   };
 
-  if constexpr (SHARED && PAIRS) {
+  {
     // The workgroup's waves read the same sub-tiles, so each pair is loaded
     // once: its K and V (16 rows of D/8 chunks of 16 bytes each, per
     // sub-tile, contiguous in the pool) come in as 64 * D/8 chunks, D/32 per
@@ -451,67 +347,6 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
       step(q, 0, std::true_type{});
       if (q + 1 < npair_wg) step(q + 1, 1, std::true_type{});
     }
-  } else if constexpr (PAIRS) {
-    // S pairs in flight.  Pair q is sub-tiles 2q and 2q+1; a pair with a
-    // masked sub-tile runs the causal variant, so does the last pair when it
-    // has a single sub-tile (its second one, past the wave's last position,
-    // is a masked copy of the last).
-    const int npair = (nsub + 1) >> 1;
-    const int upair = unmasked >> 1;
-    Tile<D> t[2 * S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      load(2 * i, t[2 * i]);
-      load(2 * i + 1, t[2 * i + 1]);
-    }
-    const int n_pad = (npair + S - 1) / S * S;
-    int qb = 0;
-    for (; qb + S <= upair && qb + S < n_pad; qb += S) {
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        compute2(qb + i, t[2 * i], t[2 * i + 1], std::false_type{});
-        load(2 * (qb + i + S), t[2 * i]);
-        load(2 * (qb + i + S) + 1, t[2 * i + 1]);
-      }
-    }
-    for (; qb + S < n_pad; qb += S) {
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        compute2(qb + i, t[2 * i], t[2 * i + 1], std::true_type{});
-        load(2 * (qb + i + S), t[2 * i]);
-        load(2 * (qb + i + S) + 1, t[2 * i + 1]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (qb + i < npair) compute2(qb + i, t[2 * i], t[2 * i + 1], std::true_type{});
-  } else {
-    Tile<D> t[S];
-#pragma unroll
-    for (int i = 0; i < S; ++i) load(i, t[i]);
-    const int n_pad = (nsub + S - 1) / S * S;
-    int kb = 0;
-    // Rounds before the first sub-tile that some column must not fully see
-    // run without the causal mask, the rest with it: two loops rather than a
-    // choice per step, whose merging paths cost register copies of every
-    // accumulator.
-    for (; kb + S <= unmasked && kb + S < n_pad; kb += S) {
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        compute(kb + i, t[i], std::false_type{});
-        load(kb + i + S, t[i]);
-      }
-    }
-    for (; kb + S < n_pad; kb += S) {
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        compute(kb + i, t[i], std::true_type{});
-        load(kb + i + S, t[i]);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < S; ++i)
-      if (kb + i < nsub) compute(kb + i, t[i], std::true_type{});
   }
 
   // lane (kg, r) holds rows 4kg+i of O^T for column r: dims (4kg+i)*JV + j
@@ -541,15 +376,14 @@ __global__ __launch_bounds__(NW * kWave, PrefillShape<D>::kBlocksPerCu) void pre
 
 template <typename T, int D, int G>
 hipError_t launch_t(const PrefillParams& p, hipStream_t stream) {
-  constexpr int CG = PrefillShape<D>::kGroups, S = PrefillShape<D>::kDepth, NW = kPrefillWaves;
-  constexpr bool PAIRS = PrefillShape<D>::kPairs;
+  constexpr int CG = PrefillShape<D>::kGroups, NW = kPrefillWaves;
   const int per_wg = NW * CG * (16 / G);
   PrefillParams q = p;
   q.chunks = (p.max_query_len + per_wg - 1) / per_wg;
   const int64_t items = static_cast<int64_t>(p.num_seqs) * q.chunks * p.num_kv_heads;
   if (items == 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG, S, PAIRS, PrefillShape<D>::kShared>),
+  hipLaunchKernelGGL((prefill_mfma_kernel<T, D, G, NW, CG>),
                      dim3(static_cast<unsigned>(items)), dim3(NW * kWave),
                      0, stream, q);
   return hipGetLastError();
