@@ -184,13 +184,14 @@ def test_prefill_parity_benchmark_batch_sampled():
     print(f"benchmark batch: {len(rows)} sampled rows, max|err| {e:.2e} (ratio {r:.3f})", flush=True)
 
 
-def test_prefill_long_prompt_sampled():
-    """A 32,768-token context whose last 16,384 tokens are new (the first half a cached
-    prefix) beside a short prompt, at the benchmark's shape: sampled rows (first, last,
-    the rows at every 4,096th new token and random ones) against the decode oracle over
-    p + 1 positions."""
-    lens, new = [32768, 40], [16384, 40]
-    wl, q, k_new, v_new, qs, slots = _setup(32, 8, 64, 16, lens, new, "bf16", seed=32768)
+@pytest.mark.parametrize("Hq,Hkv,D,dtype,L", [(32, 8, 64, "bf16", 32768), (16, 16, 128, "fp16", 16384)])
+def test_prefill_long_prompt_sampled(Hq, Hkv, D, dtype, L):
+    """A long context (32,768 tokens at the benchmark's shape, 16,384 at head_dim 128 with
+    one q head per kv head) whose second half is new (the first half a cached prefix)
+    beside a short prompt: sampled rows (first, last, the rows at every 4,096th new token
+    and random ones) against the decode oracle over p + 1 positions."""
+    lens, new = [L, 40], [L // 2, 40]
+    wl, q, k_new, v_new, qs, slots = _setup(Hq, Hkv, D, 16, lens, new, dtype, seed=L + D)
     kc, vc = _oracle_pools(wl, k_new, v_new, slots)
     c = wl.cfg
     got = _gpu(wl, q, k_new, v_new, qs, slots, max(new))
